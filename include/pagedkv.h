@@ -1,0 +1,205 @@
+/*
+ * pagedkv.h — C ABI of the paged-KV decode library for AMD Instinct MI355X (gfx950).
+ *
+ * What it computes
+ *   - kv_cache_write*: the slot scatter that stores each step's new K/V rows into
+ *     a block-paged cache ("The KV Cache" (metalworking), layout paragraph: the
+ *     reshape_and_cache kernel; "How the Paged KV Cache Works in MTPLX",
+ *     Physical Layout and Memory Organization: 4-D cache
+ *     [num_blocks, block_size, num_kv_heads, head_dim], 16 tokens per block).
+ *   - paged_attention_decode*: softmax attention of a block of q_len new query
+ *     tokens over the cache of each sequence, resolved through an int32 block
+ *     table ("The KV Cache", layout paragraph: fixed-size blocks plus an
+ *     indirection table).  Query head h reads KV head h / gqa_factor ("The KV
+ *     Cache", arithmetic paragraph, the GQA stride trick).  The split-KV form
+ *     partitions each sequence and merges the partitions by log-sum-exp
+ *     ("The KV Cache", layout paragraph: split-KV decode kernels for
+ *     single-user decode; mlxcel "KV Cache", Paged Decode Storage and Kernels:
+ *     a decode split count).
+ *   - *_k8v4: the same over a cache holding int8 K (one fp16 scale per token and
+ *     KV head) and packed 4-bit V (fp16 scale and zero per 32 elements)
+ *     ("The KV Cache", the K/V asymmetry paragraph: K8/V4).
+ *
+ * Conventions shared by every entry point
+ *   - Ownership: the caller allocates and owns every buffer, including the
+ *     split-KV workspace.  The library never allocates, frees or synchronises.
+ *   - Pointers: device pointers unless stated; all tensors dense, row-major, and
+ *     16-byte aligned.  `stream` is a hipStream_t (NULL = the null stream); all
+ *     work is enqueued on it, asynchronously, in stream order.
+ *   - Errors: every call returns PKV_OK (0) or a negative PKV_ERR_* code.  On an
+ *     error nothing is launched and pkv_last_error() (thread-local, static
+ *     storage, valid until the next call on that thread) describes it.
+ *   - Lengths: context_lens[b] counts the tokens of sequence b after this step's
+ *     q_len tokens were written (write first, then attend: "How MTPLX Manages
+ *     Memory Using Request-Sized Paged KV Cache", Request-Sized Offset
+ *     Tracking).  Query row i of a q_len block sees positions
+ *     0 .. context_lens[b] - q_len + i (causal inside the block, as in a
+ *     speculative verify block: mlxcel "KV Cache", Matrix-Absorbed MLA Decode).
+ *     Rows that see no position produce zeros.
+ *   - Device-side values are not range-checked by a host sync.  Instead the
+ *     kernels treat them safely: a length is clamped to
+ *     [0, max_blocks_per_seq * block_size]; a block-table entry outside
+ *     [0, num_blocks) drops its 16 positions from the softmax; a slot that is
+ *     negative or >= num_blocks * block_size is not written.  Duplicate slots in
+ *     one write call are undefined (the caller never issues them).
+ *   - Supported shapes: block_size == 16; head_dim 64 or 128;
+ *     num_q_heads % gqa_factor == 0; 1 <= gqa_factor * q_len <= 16.  Anything
+ *     else returns PKV_ERR_UNSUPPORTED.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+enum {
+  PKV_F16 = 0,   /* IEEE binary16 */
+  PKV_BF16 = 1,  /* bfloat16 */
+  PKV_F32 = 2    /* float32: only for `out` */
+};
+
+/* cache formats for kv_cache_bytes_per_token */
+enum {
+  PKV_FMT_F16 = 0,
+  PKV_FMT_BF16 = 1,
+  PKV_FMT_K8V4 = 3
+};
+
+/* return codes */
+enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = -1,         /* a required pointer is NULL */
+  PKV_ERR_SHAPE = -2,        /* a size is negative or inconsistent */
+  PKV_ERR_UNSUPPORTED = -3,  /* a valid but unsupported configuration */
+  PKV_ERR_WORKSPACE = -4,    /* split-KV workspace missing or too small */
+  PKV_ERR_LAUNCH = -5,       /* the HIP runtime rejected a launch */
+  PKV_ERR_ALIGN = -6         /* a pointer is not 16-byte aligned */
+};
+
+/* Text of the last error on this thread ("" after a successful call). */
+const char* pkv_last_error(void);
+
+/* Library ABI version (major * 100 + minor). */
+int pkv_version(void);
+
+/*
+ * kv_cache_write — reshape_and_cache slot scatter for fp16/bf16 caches.
+ *   key, value:   [num_tokens, num_kv_heads, head_dim] of `dtype`
+ *   key_cache, value_cache: [num_blocks, block_size, num_kv_heads, head_dim] of `dtype`
+ *   slot_mapping: int64 [num_tokens]; token t goes to block slot/16, row slot%16.
+ *                 Negative or out-of-pool slots are skipped.
+ * The copy is bit-exact.  num_tokens == 0 is a no-op.
+ */
+int kv_cache_write(const void* key, const void* value, void* key_cache, void* value_cache,
+                   const int64_t* slot_mapping, int64_t num_tokens, int num_kv_heads,
+                   int head_dim, int block_size, int64_t num_blocks, int dtype, void* stream);
+
+/*
+ * paged_attention_decode — one workgroup per (sequence, KV head), no workspace.
+ *   out:          [batch, q_len, num_q_heads, head_dim] of out_dtype (f16, bf16 or f32)
+ *   query:        [batch, q_len, num_q_heads, head_dim] of kv_dtype
+ *   key_cache, value_cache: [num_blocks, block_size, num_kv_heads, head_dim] of kv_dtype
+ *   block_tables: int32 [batch, max_blocks_per_seq]; only the first
+ *                 ceil(len/block_size) entries of a row are read
+ *   context_lens: int32 [batch]
+ *   num_kv_heads = num_q_heads / gqa_factor.  scale multiplies q.k.
+ * Accumulation is fp32; the output is rounded to nearest-even once.
+ */
+int paged_attention_decode(void* out, int out_dtype, const void* query,
+                           const void* key_cache, const void* value_cache, int kv_dtype,
+                           const int32_t* block_tables, int max_blocks_per_seq,
+                           const int32_t* context_lens, int batch, int q_len, int num_q_heads,
+                           int gqa_factor, int head_dim, int block_size, int64_t num_blocks,
+                           float scale, void* stream);
+
+/*
+ * Workspace bytes for the split-KV calls (host-only arithmetic, no GPU use).
+ * partition_size is in tokens and must be a positive multiple of block_size
+ * (16).  max_context_len bounds context_lens for the grid size; a longer
+ * sequence is still handled correctly (its last partition runs to its end).
+ */
+int paged_attention_decode_splitkv_workspace_size(int batch, int q_len, int num_q_heads,
+                                                  int head_dim, int max_context_len,
+                                                  int partition_size, size_t* out_bytes);
+
+/*
+ * paged_attention_decode_splitkv — partition kernel over
+ * (partition, KV head, sequence) writing per-partition (o, max, sum) to
+ * `workspace`, then a log-sum-exp merge kernel writing `out`.  Same arguments
+ * and result as paged_attention_decode (up to fp32 summation order).  The
+ * workspace contents on entry do not matter; two calls that overlap in time
+ * must not share a workspace.
+ */
+int paged_attention_decode_splitkv(void* out, int out_dtype, const void* query,
+                                   const void* key_cache, const void* value_cache, int kv_dtype,
+                                   const int32_t* block_tables, int max_blocks_per_seq,
+                                   const int32_t* context_lens, int batch, int q_len,
+                                   int num_q_heads, int gqa_factor, int head_dim, int block_size,
+                                   int64_t num_blocks, float scale, int max_context_len,
+                                   int partition_size, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/*
+ * kv_cache_write_k8v4 — quantize-on-write into a K8/V4 cache.
+ *   key, value: [num_tokens, num_kv_heads, head_dim] of in_dtype (f16 or bf16)
+ *   k_cache int8   [num_blocks, block_size, num_kv_heads, head_dim]
+ *   k_scale fp16   [num_blocks, block_size, num_kv_heads]
+ *   v_cache uint8  [num_blocks, block_size, num_kv_heads, head_dim / 2]
+ *   v_scale, v_zero fp16 [num_blocks, block_size, num_kv_heads, head_dim / 32]
+ * Side tensors are indexed like the cache ("How MTPLX Manages Memory Using
+ * Request-Sized Paged KV Cache", Quantization-Aware Memory Layout).
+ * K per (token, head), in fp32: amax = max|k|; s = fp16_rne(amax / 127);
+ *   code = s == 0 ? 0 : clamp(rint_even(k / s), -127, 127).
+ * V per group of 32, in fp32: s = fp16_rne((max - min) / 15); z = fp16_rne(min);
+ *   code = s == 0 ? 0 : clamp(rint_even((v - z) / s), 0, 15); element 2i in the
+ *   low nibble of byte i, element 2i+1 in the high nibble.
+ * Divisions are correctly rounded, so codes and scales are bit-exact.
+ */
+int kv_cache_write_k8v4(const void* key, const void* value, int in_dtype, int8_t* k_cache,
+                        void* k_scale, uint8_t* v_cache, void* v_scale, void* v_zero,
+                        const int64_t* slot_mapping, int64_t num_tokens, int num_kv_heads,
+                        int head_dim, int block_size, int64_t num_blocks, void* stream);
+
+/*
+ * paged_attention_decode_k8v4 — paged_attention_decode over the K8/V4 arrays
+ * above, dequantizing in registers (k = code * s; v = code * s + z).
+ * query and out as in paged_attention_decode with query of q_dtype (f16/bf16).
+ */
+int paged_attention_decode_k8v4(void* out, int out_dtype, const void* query, int q_dtype,
+                                const int8_t* k_cache, const void* k_scale,
+                                const uint8_t* v_cache, const void* v_scale, const void* v_zero,
+                                const int32_t* block_tables, int max_blocks_per_seq,
+                                const int32_t* context_lens, int batch, int q_len,
+                                int num_q_heads, int gqa_factor, int head_dim, int block_size,
+                                int64_t num_blocks, float scale, void* stream);
+
+/* Split-KV form of paged_attention_decode_k8v4 (workspace as for the fp16 call). */
+int paged_attention_decode_splitkv_k8v4(void* out, int out_dtype, const void* query, int q_dtype,
+                                        const int8_t* k_cache, const void* k_scale,
+                                        const uint8_t* v_cache, const void* v_scale,
+                                        const void* v_zero, const int32_t* block_tables,
+                                        int max_blocks_per_seq, const int32_t* context_lens,
+                                        int batch, int q_len, int num_q_heads, int gqa_factor,
+                                        int head_dim, int block_size, int64_t num_blocks,
+                                        float scale, int max_context_len, int partition_size,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Cache bytes one token occupies over all layers (host-only arithmetic).
+ * "The KV Cache", arithmetic paragraph: one K and one V vector per KV head per
+ * layer; fp16/bf16: 2 * layers * kv_heads * head_dim * 2.  K8/V4:
+ * layers * kv_heads * (head_dim + 2 + head_dim/2 + 4 * head_dim/32).
+ */
+int kv_cache_bytes_per_token(int num_layers, int num_kv_heads, int head_dim, int kv_format,
+                             int64_t* out_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,27 @@
+"""Paged-KV decode for AMD Instinct MI355X (gfx950).
+
+Hand-written HIP kernels behind a C ABI (``include/pagedkv.h``): the
+reshape_and_cache slot scatter, paged-attention decode (direct and split-KV with
+a log-sum-exp merge) and their K8/V4-quantized variants.
+
+The binding (``_binding``) loads ``libpagedkv.so`` on first use of any of the
+names below and raises ImportError if the library has not been built; there is
+no fallback.  ``workloads`` (seeded synthetic inputs) needs no library.
+"""
+
+_EXPORTS = (
+    "BLOCK_SIZE", "PKV_BF16", "PKV_F16", "PKV_F32", "PKV_FMT_BF16", "PKV_FMT_F16",
+    "PKV_FMT_K8V4", "PagedKVError", "kv_cache_bytes_per_token", "kv_cache_write",
+    "kv_cache_write_k8v4", "last_error", "lib", "paged_attention_decode",
+    "paged_attention_decode_k8v4", "paged_attention_decode_splitkv",
+    "paged_attention_decode_splitkv_k8v4", "splitkv_workspace_size", "version",
+)
+
+__all__ = list(_EXPORTS)
+
+
+def __getattr__(name):
+    if name in _EXPORTS:
+        from . import _binding
+        return getattr(_binding, name)
+    raise AttributeError(name)

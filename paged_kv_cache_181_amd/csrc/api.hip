@@ -1,0 +1,319 @@
+// C ABI of the paged-KV decode library (declared in include/pagedkv.h).
+//
+// Every entry point validates its arguments on the host first (no HIP call is
+// made before validation passes), then enqueues kernels on the caller's stream.
+// Nothing is allocated, freed or synchronised here.
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <cmath>
+
+#include "../../include/pagedkv.h"
+#include "pkv_common.h"
+#include "pkv_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return PKV_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int launch_result(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int check_cache_geometry(int num_kv_heads, int head_dim, int block_size, int64_t num_blocks) {
+  if (num_kv_heads <= 0) return fail(PKV_ERR_SHAPE, "num_kv_heads must be positive");
+  if (num_blocks < 0) return fail(PKV_ERR_SHAPE, "num_blocks must be non-negative");
+  if (block_size != 16) return fail(PKV_ERR_UNSUPPORTED, "block_size must be 16 (got %d)", block_size);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  return PKV_OK;
+}
+
+// Shared validation of the attention calls; fills the kernel arguments.
+int check_attention(void* out, int out_dtype, const void* query, const void* k_cache,
+                    const void* v_cache, const int32_t* block_tables, int max_blocks,
+                    const int32_t* context_lens, int batch, int q_len, int num_q_heads,
+                    int gqa_factor, int head_dim, int block_size, int64_t num_blocks, float scale,
+                    pkv::AttnArgs& a) {
+  if (batch < 0 || q_len <= 0 || num_q_heads <= 0 || gqa_factor <= 0 || max_blocks < 0)
+    return fail(PKV_ERR_SHAPE, "batch >= 0, q_len > 0, num_q_heads > 0, gqa_factor > 0, "
+                               "max_blocks_per_seq >= 0 required");
+  if (num_q_heads % gqa_factor != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "num_q_heads (%d) must be a multiple of gqa_factor (%d)",
+                num_q_heads, gqa_factor);
+  const int hkv = num_q_heads / gqa_factor;
+  int rc = check_cache_geometry(hkv, head_dim, block_size, num_blocks);
+  if (rc) return rc;
+  if ((int64_t)gqa_factor * q_len > 16)
+    return fail(PKV_ERR_UNSUPPORTED, "gqa_factor * q_len must be <= 16 (got %d)",
+                gqa_factor * q_len);
+  if (out_dtype != PKV_F16 && out_dtype != PKV_BF16 && out_dtype != PKV_F32)
+    return fail(PKV_ERR_UNSUPPORTED, "out_dtype must be PKV_F16, PKV_BF16 or PKV_F32");
+  if (!std::isfinite(scale)) return fail(PKV_ERR_SHAPE, "scale must be finite");
+  if (batch > 65535 || hkv > 65535) return fail(PKV_ERR_UNSUPPORTED, "batch or KV heads too large");
+  if (batch == 0) return PKV_OK;
+  if (!out || !query || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PKV_ERR_NULL, "a required pointer is NULL");
+  if (!aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_ALIGN, "query and caches must be 16-byte aligned");
+  if (num_blocks == 0 || max_blocks == 0)
+    return fail(PKV_ERR_SHAPE, "num_blocks and max_blocks_per_seq must be positive when batch > 0");
+  a = pkv::AttnArgs{};
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.q = query;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.max_blocks = max_blocks;
+  a.batch = batch;
+  a.q_len = q_len;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = hkv;
+  a.gqa = gqa_factor;
+  a.num_blocks = num_blocks;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  a.part_blocks = max_blocks;
+  a.num_parts = 1;
+  return PKV_OK;
+}
+
+int split_geometry(int batch, int q_len, int num_q_heads, int head_dim, int max_context_len,
+                   int partition_size, int64_t& parts, size_t& bytes) {
+  if (batch < 0 || q_len <= 0 || num_q_heads <= 0 || max_context_len < 0)
+    return fail(PKV_ERR_SHAPE, "invalid split-KV sizes");
+  if (partition_size <= 0 || partition_size % 16 != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "partition_size must be a positive multiple of 16 (got %d)",
+                partition_size);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  parts = ((int64_t)max_context_len + partition_size - 1) / partition_size;
+  if (parts < 1) parts = 1;
+  if (parts > 65535) return fail(PKV_ERR_UNSUPPORTED, "too many partitions (%lld)", (long long)parts);
+  const int64_t rows = (int64_t)batch * q_len * num_q_heads;
+  bytes = (size_t)(rows * parts * (head_dim + 2) * 4);
+  return PKV_OK;
+}
+
+int setup_split(pkv::AttnArgs& a, int head_dim, int max_context_len, int partition_size,
+                void* workspace, size_t workspace_bytes) {
+  int64_t parts = 0;
+  size_t need = 0;
+  int rc = split_geometry(a.batch, a.q_len, a.num_q_heads, head_dim, max_context_len,
+                          partition_size, parts, need);
+  if (rc) return rc;
+  if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(PKV_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed",
+                workspace_bytes, need);
+  const int64_t rows = (int64_t)a.batch * a.q_len * a.num_q_heads;
+  a.num_parts = (int)parts;
+  a.part_blocks = partition_size / 16;
+  a.ws_o = (float*)workspace;
+  a.ws_m = a.ws_o + rows * parts * head_dim;
+  a.ws_l = a.ws_m + rows * parts;
+  return PKV_OK;
+}
+
+int check_k8v4_pointers(const void* k_scale, const void* v_scale, const void* v_zero) {
+  if (!k_scale || !v_scale || !v_zero) return fail(PKV_ERR_NULL, "K8/V4 scale arrays are NULL");
+  if ((reinterpret_cast<uintptr_t>(k_scale) & 1u) || (reinterpret_cast<uintptr_t>(v_scale) & 7u) ||
+      (reinterpret_cast<uintptr_t>(v_zero) & 7u))
+    return fail(PKV_ERR_ALIGN, "k_scale must be 2-byte and v_scale/v_zero 8-byte aligned");
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_err; }
+
+int pkv_version(void) { return 100; }
+
+int kv_cache_bytes_per_token(int num_layers, int num_kv_heads, int head_dim, int kv_format,
+                             int64_t* out_bytes) {
+  if (!out_bytes) return fail(PKV_ERR_NULL, "out_bytes is NULL");
+  if (num_layers < 0 || num_kv_heads < 0 || head_dim < 0)
+    return fail(PKV_ERR_SHAPE, "sizes must be non-negative");
+  const int64_t lh = (int64_t)num_layers * num_kv_heads;
+  if (kv_format == PKV_FMT_F16 || kv_format == PKV_FMT_BF16) {
+    *out_bytes = 2 * lh * head_dim * 2;
+  } else if (kv_format == PKV_FMT_K8V4) {
+    if (head_dim % 32) return fail(PKV_ERR_UNSUPPORTED, "K8/V4 needs head_dim % 32 == 0");
+    *out_bytes = lh * (head_dim + 2 + head_dim / 2 + 4 * (head_dim / 32));
+  } else {
+    return fail(PKV_ERR_UNSUPPORTED, "unknown kv_format %d", kv_format);
+  }
+  return ok();
+}
+
+int kv_cache_write(const void* key, const void* value, void* key_cache, void* value_cache,
+                   const int64_t* slot_mapping, int64_t num_tokens, int num_kv_heads,
+                   int head_dim, int block_size, int64_t num_blocks, int dtype, void* stream) {
+  if (num_tokens < 0) return fail(PKV_ERR_SHAPE, "num_tokens must be non-negative");
+  int rc = check_cache_geometry(num_kv_heads, head_dim, block_size, num_blocks);
+  if (rc) return rc;
+  if (dtype != PKV_F16 && dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "dtype must be PKV_F16 or PKV_BF16");
+  if (num_tokens > 0x7fffffff) return fail(PKV_ERR_UNSUPPORTED, "too many tokens");
+  if (num_tokens == 0 || num_blocks == 0) return ok();
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+    return fail(PKV_ERR_NULL, "a required pointer is NULL");
+  if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache))
+    return fail(PKV_ERR_ALIGN, "key, value and caches must be 16-byte aligned");
+  return launch_result(pkv::launch_kv_write(key, value, key_cache, value_cache, slot_mapping,
+                                            num_tokens, num_kv_heads, head_dim, num_blocks,
+                                            (hipStream_t)stream),
+                       "kv_cache_write");
+}
+
+int kv_cache_write_k8v4(const void* key, const void* value, int in_dtype, int8_t* k_cache,
+                        void* k_scale, uint8_t* v_cache, void* v_scale, void* v_zero,
+                        const int64_t* slot_mapping, int64_t num_tokens, int num_kv_heads,
+                        int head_dim, int block_size, int64_t num_blocks, void* stream) {
+  if (num_tokens < 0) return fail(PKV_ERR_SHAPE, "num_tokens must be non-negative");
+  int rc = check_cache_geometry(num_kv_heads, head_dim, block_size, num_blocks);
+  if (rc) return rc;
+  if (in_dtype != PKV_F16 && in_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "in_dtype must be PKV_F16 or PKV_BF16");
+  if (num_tokens * num_kv_heads > 0x7fffffffLL * 4)
+    return fail(PKV_ERR_UNSUPPORTED, "too many tokens");
+  if (num_tokens == 0 || num_blocks == 0) return ok();
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+    return fail(PKV_ERR_NULL, "a required pointer is NULL");
+  rc = check_k8v4_pointers(k_scale, v_scale, v_zero);
+  if (rc) return rc;
+  return launch_result(pkv::launch_kv_write_k8v4(key, value, in_dtype, k_cache, k_scale, v_cache,
+                                                 v_scale, v_zero, slot_mapping, num_tokens,
+                                                 num_kv_heads, head_dim, num_blocks,
+                                                 (hipStream_t)stream),
+                       "kv_cache_write_k8v4");
+}
+
+int paged_attention_decode(void* out, int out_dtype, const void* query, const void* key_cache,
+                           const void* value_cache, int kv_dtype, const int32_t* block_tables,
+                           int max_blocks_per_seq, const int32_t* context_lens, int batch,
+                           int q_len, int num_q_heads, int gqa_factor, int head_dim,
+                           int block_size, int64_t num_blocks, float scale, void* stream) {
+  if (kv_dtype != PKV_F16 && kv_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "kv_dtype must be PKV_F16 or PKV_BF16");
+  pkv::AttnArgs a{};
+  int rc = check_attention(out, out_dtype, query, key_cache, value_cache, block_tables,
+                           max_blocks_per_seq, context_lens, batch, q_len, num_q_heads, gqa_factor,
+                           head_dim, block_size, num_blocks, scale, a);
+  if (rc) return rc;
+  if (batch == 0) return ok();
+  return launch_result(pkv::launch_attention(a, kv_dtype, kv_dtype, head_dim, (hipStream_t)stream),
+                       "paged_attention_decode");
+}
+
+int paged_attention_decode_splitkv_workspace_size(int batch, int q_len, int num_q_heads,
+                                                  int head_dim, int max_context_len,
+                                                  int partition_size, size_t* out_bytes) {
+  if (!out_bytes) return fail(PKV_ERR_NULL, "out_bytes is NULL");
+  int64_t parts = 0;
+  size_t bytes = 0;
+  int rc = split_geometry(batch, q_len, num_q_heads, head_dim, max_context_len, partition_size,
+                          parts, bytes);
+  if (rc) return rc;
+  *out_bytes = bytes;
+  return ok();
+}
+
+int paged_attention_decode_splitkv(void* out, int out_dtype, const void* query,
+                                   const void* key_cache, const void* value_cache, int kv_dtype,
+                                   const int32_t* block_tables, int max_blocks_per_seq,
+                                   const int32_t* context_lens, int batch, int q_len,
+                                   int num_q_heads, int gqa_factor, int head_dim, int block_size,
+                                   int64_t num_blocks, float scale, int max_context_len,
+                                   int partition_size, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  if (kv_dtype != PKV_F16 && kv_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "kv_dtype must be PKV_F16 or PKV_BF16");
+  pkv::AttnArgs a{};
+  int rc = check_attention(out, out_dtype, query, key_cache, value_cache, block_tables,
+                           max_blocks_per_seq, context_lens, batch, q_len, num_q_heads, gqa_factor,
+                           head_dim, block_size, num_blocks, scale, a);
+  if (rc) return rc;
+  if (batch == 0) return ok();
+  rc = setup_split(a, head_dim, max_context_len, partition_size, workspace, workspace_bytes);
+  if (rc) return rc;
+  return launch_result(pkv::launch_attention(a, kv_dtype, kv_dtype, head_dim, (hipStream_t)stream),
+                       "paged_attention_decode_splitkv");
+}
+
+int paged_attention_decode_k8v4(void* out, int out_dtype, const void* query, int q_dtype,
+                                const int8_t* k_cache, const void* k_scale,
+                                const uint8_t* v_cache, const void* v_scale, const void* v_zero,
+                                const int32_t* block_tables, int max_blocks_per_seq,
+                                const int32_t* context_lens, int batch, int q_len,
+                                int num_q_heads, int gqa_factor, int head_dim, int block_size,
+                                int64_t num_blocks, float scale, void* stream) {
+  if (q_dtype != PKV_F16 && q_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "q_dtype must be PKV_F16 or PKV_BF16");
+  pkv::AttnArgs a{};
+  int rc = check_attention(out, out_dtype, query, k_cache, v_cache, block_tables,
+                           max_blocks_per_seq, context_lens, batch, q_len, num_q_heads, gqa_factor,
+                           head_dim, block_size, num_blocks, scale, a);
+  if (rc) return rc;
+  if (batch == 0) return ok();
+  rc = check_k8v4_pointers(k_scale, v_scale, v_zero);
+  if (rc) return rc;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.v_zero = v_zero;
+  return launch_result(pkv::launch_attention(a, PKV_FMT_K8V4, q_dtype, head_dim,
+                                             (hipStream_t)stream),
+                       "paged_attention_decode_k8v4");
+}
+
+int paged_attention_decode_splitkv_k8v4(void* out, int out_dtype, const void* query, int q_dtype,
+                                        const int8_t* k_cache, const void* k_scale,
+                                        const uint8_t* v_cache, const void* v_scale,
+                                        const void* v_zero, const int32_t* block_tables,
+                                        int max_blocks_per_seq, const int32_t* context_lens,
+                                        int batch, int q_len, int num_q_heads, int gqa_factor,
+                                        int head_dim, int block_size, int64_t num_blocks,
+                                        float scale, int max_context_len, int partition_size,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (q_dtype != PKV_F16 && q_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "q_dtype must be PKV_F16 or PKV_BF16");
+  pkv::AttnArgs a{};
+  int rc = check_attention(out, out_dtype, query, k_cache, v_cache, block_tables,
+                           max_blocks_per_seq, context_lens, batch, q_len, num_q_heads, gqa_factor,
+                           head_dim, block_size, num_blocks, scale, a);
+  if (rc) return rc;
+  if (batch == 0) return ok();
+  rc = check_k8v4_pointers(k_scale, v_scale, v_zero);
+  if (rc) return rc;
+  rc = setup_split(a, head_dim, max_context_len, partition_size, workspace, workspace_bytes);
+  if (rc) return rc;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.v_zero = v_zero;
+  return launch_result(pkv::launch_attention(a, PKV_FMT_K8V4, q_dtype, head_dim,
+                                             (hipStream_t)stream),
+                       "paged_attention_decode_splitkv_k8v4");
+}
+
+}  // extern "C"

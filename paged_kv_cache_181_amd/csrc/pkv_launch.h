@@ -1,0 +1,45 @@
+// Host-side launchers of the HIP kernels (internal; the public ABI is pagedkv.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+hipError_t launch_kv_write(const void* key, const void* value, void* key_cache, void* value_cache,
+                           const int64_t* slots, int64_t num_tokens, int num_kv_heads,
+                           int head_dim, int64_t num_blocks, hipStream_t stream);
+
+hipError_t launch_kv_write_k8v4(const void* key, const void* value, int in_dtype, int8_t* k_cache,
+                                void* k_scale, uint8_t* v_cache, void* v_scale, void* v_zero,
+                                const int64_t* slots, int64_t num_tokens, int num_kv_heads,
+                                int head_dim, int64_t num_blocks, hipStream_t stream);
+
+// Everything the attention kernels need; filled by the ABI layer after validation.
+struct AttnArgs {
+  void* out;
+  int out_dtype;                 // OutT
+  const void* q;                 // [B, Q, Hq, D] 16-bit
+  const void* k_cache;           // [NB, 16, Hkv, D] (16-bit or int8 codes)
+  const void* v_cache;           // [NB, 16, Hkv, D] 16-bit, or [NB, 16, Hkv, D/2] packed 4-bit
+  const void* k_scale;           // K8/V4 only: fp16 [NB, 16, Hkv]
+  const void* v_scale;           // K8/V4 only: fp16 [NB, 16, Hkv, D/32]
+  const void* v_zero;            // K8/V4 only: fp16 [NB, 16, Hkv, D/32]
+  const int32_t* block_tables;   // [B, max_blocks]
+  const int32_t* context_lens;   // [B]
+  int max_blocks;
+  int batch, q_len, num_q_heads, num_kv_heads, gqa;
+  int64_t num_blocks;
+  float scale_log2;              // softmax scale * log2(e)
+  int part_blocks;               // cache blocks per partition
+  int num_parts;                 // partitions in the grid (1 = direct form)
+  float* ws_o;                   // split form: [B*Q*Hq, P, D] unnormalised partial outputs
+  float* ws_m;                   // split form: [B*Q*Hq, P] running max (log2 units)
+  float* ws_l;                   // split form: [B*Q*Hq, P] softmax denominators
+};
+
+// kv_fmt: 0 f16, 1 bf16, 3 k8v4; q_fmt: 0 f16, 1 bf16 (must equal kv_fmt unless k8v4).
+hipError_t launch_attention(const AttnArgs& a, int kv_fmt, int q_fmt, int head_dim,
+                            hipStream_t stream);
+
+}  // namespace pkv

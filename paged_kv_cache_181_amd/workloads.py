@@ -33,9 +33,15 @@ def f32_to_bits(x: np.ndarray, fmt: str) -> np.ndarray:
     if fmt == "f16":
         return x.astype(np.float16).view(np.uint16)
     if fmt == "bf16":
-        u = x.view(np.uint32).astype(np.uint64)
-        bias = ((u >> np.uint64(16)) & np.uint64(1)) + np.uint64(0x7FFF)
-        return ((u + bias) >> np.uint64(16)).astype(np.uint16)
+        u = x.view(np.uint32)
+        # nearest-even: add 0x7FFF plus the lowest kept bit, then truncate
+        # (finite inputs only: the sum cannot wrap)
+        t = u >> np.uint32(16)
+        t &= np.uint32(1)
+        t += np.uint32(0x7FFF)
+        t += u
+        t >>= np.uint32(16)
+        return t.astype(np.uint16)
     raise ValueError(fmt)
 
 
@@ -101,14 +107,18 @@ def build_tables(rng, blocks_needed, num_blocks, max_blocks=None):
 
 def fill_pool(rng, tables, blocks_needed, num_blocks, num_kv_heads, head_dim, fmt):
     """K and V pools with ~N(0,1) values in every referenced block (all 16 rows,
-    so rows past a sequence's length hold ordinary values); other blocks are 0."""
+    so rows past a sequence's length hold ordinary values); other blocks are 0.
+    K is drawn for all referenced blocks (in table order), then V."""
     shape = (num_blocks, BLOCK_SIZE, num_kv_heads, head_dim)
     used = np.concatenate([tables[b, :n] for b, n in enumerate(blocks_needed)]) \
         if len(blocks_needed) else np.zeros(0, np.int32)
     kc = np.zeros(shape, dtype=np.uint16)
     vc = np.zeros(shape, dtype=np.uint16)
-    kc[used] = normal_bits(rng, (len(used),) + shape[1:], fmt)
-    vc[used] = normal_bits(rng, (len(used),) + shape[1:], fmt)
+    chunk = 2048
+    for pool in (kc, vc):
+        for s in range(0, len(used), chunk):
+            ids = used[s:s + chunk]
+            pool[ids] = normal_bits(rng, (len(ids),) + shape[1:], fmt)
     return kc, vc
 
 

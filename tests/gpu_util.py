@@ -1,0 +1,100 @@
+"""Helpers for the GPU tests: upload seeded cases and call the library."""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from paged_kv_cache_181_amd import workloads as W
+
+TOL = 2e-3          # max-abs error bound for fp16/bf16 K/V with fp32 accumulation
+
+
+def tdtype(fmt):
+    return {"f16": torch.float16, "bf16": torch.bfloat16}[fmt]
+
+
+def bits_to_dev(bits: np.ndarray, fmt: str, dev="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(tdtype(fmt))
+
+
+def dev_to_bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+class DevCase:
+    """A PagedCase mirrored on the GPU."""
+
+    def __init__(self, case: W.PagedCase, dev="cuda"):
+        self.case = case
+        self.k = bits_to_dev(case.key_cache, case.fmt, dev)
+        self.v = bits_to_dev(case.value_cache, case.fmt, dev)
+        self.q = bits_to_dev(case.query, case.fmt, dev)
+        self.bt = torch.from_numpy(case.block_tables).to(dev)
+        self.cl = torch.from_numpy(case.context_lens).to(dev)
+        self.new_k = bits_to_dev(case.new_key, case.fmt, dev)
+        self.new_v = bits_to_dev(case.new_value, case.fmt, dev)
+        self.slots = torch.from_numpy(case.slot_mapping).to(dev)
+
+
+def run_decode(P, dc: DevCase, *, split: bool, partition_size=512, out_dtype=torch.float32,
+               max_context_len=None, q=None, cl=None, bt=None, k=None, v=None):
+    c = dc.case
+    q = dc.q if q is None else q
+    cl = dc.cl if cl is None else cl
+    bt = dc.bt if bt is None else bt
+    k = dc.k if k is None else k
+    v = dc.v if v is None else v
+    out = torch.full(q.shape, float("nan"), dtype=out_dtype, device=q.device)
+    if split:
+        mcl = int(cl.max().item()) if max_context_len is None else max_context_len
+        nbytes = P.splitkv_workspace_size(q.shape[0], q.shape[1], q.shape[2], q.shape[3], mcl,
+                                          partition_size)
+        ws = torch.empty(max(nbytes, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+        P.paged_attention_decode_splitkv(out, q, k, v, bt, cl, c.scale, c.gqa_factor, mcl,
+                                         partition_size, ws)
+    else:
+        P.paged_attention_decode(out, q, k, v, bt, cl, c.scale, c.gqa_factor)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_decode(case: W.PagedCase):
+    return oracle.paged_attention(case.query, case.key_cache, case.value_cache, case.block_tables,
+                                  case.context_lens, case.scale, case.gqa_factor, case.fmt)
+
+
+def max_err(gpu_out: torch.Tensor, ref: np.ndarray) -> float:
+    got = gpu_out.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all(), "non-finite output"
+    return float(np.abs(got - ref).max()) if ref.size else 0.0
+
+
+def k8v4_pool(nb, hkv, d, dev="cuda"):
+    return dict(
+        k_cache=torch.zeros((nb, 16, hkv, d), dtype=torch.int8, device=dev),
+        k_scale=torch.zeros((nb, 16, hkv), dtype=torch.float16, device=dev),
+        v_cache=torch.zeros((nb, 16, hkv, d // 2), dtype=torch.uint8, device=dev),
+        v_scale=torch.zeros((nb, 16, hkv, d // 32), dtype=torch.float16, device=dev),
+        v_zero=torch.zeros((nb, 16, hkv, d // 32), dtype=torch.float16, device=dev),
+    )
+
+
+def k8v4_np(pool):
+    return (pool["k_cache"].cpu().numpy(), pool["k_scale"].cpu().numpy(),
+            pool["v_cache"].cpu().numpy(), pool["v_scale"].cpu().numpy(),
+            pool["v_zero"].cpu().numpy())
+
+
+def oracle_k8v4_pool(case: W.PagedCase):
+    """Quantize every referenced cache row with the oracle (slot order)."""
+    nb, hkv, d = case.num_blocks, case.num_kv_heads, case.head_dim
+    arrs = (np.zeros((nb, 16, hkv, d), np.int8), np.zeros((nb, 16, hkv), np.float16),
+            np.zeros((nb, 16, hkv, d // 2), np.uint8), np.zeros((nb, 16, hkv, d // 32), np.float16),
+            np.zeros((nb, 16, hkv, d // 32), np.float16))
+    used = np.unique(case.block_tables[case.block_tables >= 0])
+    slots = (used[:, None] * 16 + np.arange(16)[None]).reshape(-1).astype(np.int64)
+    k = case.key_cache[used].reshape(-1, hkv, d)
+    v = case.value_cache[used].reshape(-1, hkv, d)
+    return oracle.kv_cache_write_k8v4(k, v, case.fmt, *arrs, slots), slots, k, v
