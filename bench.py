@@ -1,0 +1,357 @@
+#!/usr/bin/env python3
+"""Paged-decode benchmark on one MI355X.
+
+Headline workload: single-user long-context split-KV decode.  One step is one
+decoded token through 32 layers; per layer it writes the new token's K/V into
+that layer's block-paged cache (kv_cache_write) and runs split-KV paged
+attention over the 32768-token context (partition 512: partition kernel + log-
+sum-exp merge).  Batch 1, q_len 1, 32 query / 8 KV heads, head_dim 128, fp16,
+2048 blocks of 16 per layer in a randomly permuted pool, one block table shared
+by the layers.  32 distinct layer caches (4 GiB) keep the working set far
+beyond the 256 MB Infinity Cache.
+
+value = KV bytes streamed per step (32 x 128 MiB) / step time, with all inputs
+resident in HBM.  The dominant kernel's roofline entry uses HIP events around
+each partition-kernel launch on the launch stream, in a second pass of the same
+steps (the headline pass carries no per-launch events).
+
+python bench.py [--steps K] [--warmup W] [--no-extra] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged-decode KV-stream GB/s (% of 8 TB/s HBM) + us/layer at 32K ctx"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attn_partition_long32k.json")
+KERNEL_SOURCES = ["paged_kv_cache_181_amd/csrc/attn_kernels.hip",
+                  "paged_kv_cache_181_amd/csrc/pkv_common.h"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--partition", type=int, default=512)
+    ap.add_argument("--seed", type=int, default=3)
+    ap.add_argument("--no-extra", action="store_true", help="skip the other four workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------
+
+class Long32K:
+    """Headline: batch 1, 32K context, 32 layers, split-KV decode."""
+    name = "long32k"
+
+    def __init__(self, P, W, torch, layers, partition, seed):
+        import numpy as np
+        self.P, self.torch, self.layers, self.partition = P, torch, layers, partition
+        dev = torch.device("cuda:0")
+        case = W.long32k(seed)
+        self.case = case
+        self.L = int(case.context_lens[0])
+        self.hq, self.hkv, self.d = case.num_q_heads, case.num_kv_heads, case.head_dim
+        self.nb = case.num_blocks
+        up = lambda b: torch.from_numpy(b.view(np.int16)).to(dev).view(torch.float16)  # noqa: E731
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(seed * 1000)
+        shape = (self.nb, 16, self.hkv, self.d)
+        self.K, self.V, self.q, self.nk, self.nv = [], [], [], [], []
+        for l in range(layers):
+            if l == 0:          # the parity-tested seeded case, byte for byte
+                self.K.append(up(case.key_cache))
+                self.V.append(up(case.value_cache))
+                self.q.append(up(case.query))
+                self.nk.append(up(case.new_key))
+                self.nv.append(up(case.new_value))
+            else:
+                self.K.append(torch.randn(shape, generator=gen, device=dev, dtype=torch.float16))
+                self.V.append(torch.randn(shape, generator=gen, device=dev, dtype=torch.float16))
+                self.q.append(torch.randn(case.query.shape, generator=gen, device=dev,
+                                          dtype=torch.float16))
+                self.nk.append(torch.randn(case.new_key.shape, generator=gen, device=dev,
+                                           dtype=torch.float16))
+                self.nv.append(torch.randn(case.new_value.shape, generator=gen, device=dev,
+                                           dtype=torch.float16))
+        self.bt = torch.from_numpy(case.block_tables).to(dev)
+        self.cl = torch.from_numpy(case.context_lens).to(dev)
+        self.slots = torch.from_numpy(case.slot_mapping).to(dev)
+        self.out = [torch.empty(case.query.shape, dtype=torch.float16, device=dev)
+                    for _ in range(layers)]
+        nbytes = P.splitkv_workspace_size(1, 1, self.hq, self.d, self.L, partition)
+        self.ws = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+        # algorithmic KV bytes one layer must read: K and V rows of every position
+        self.layer_bytes = self.L * self.hkv * self.d * 2 * 2
+        self.step_bytes = self.layer_bytes * layers
+
+    def step(self):
+        P, c = self.P, self.case
+        for l in range(self.layers):
+            P.kv_cache_write(self.nk[l], self.nv[l], self.K[l], self.V[l], self.slots)
+            P.paged_attention_decode_splitkv(self.out[l], self.q[l], self.K[l], self.V[l], self.bt,
+                                             self.cl, c.scale, c.gqa_factor, self.L,
+                                             self.partition, self.ws)
+
+    def step_timed_kernels(self, ev):
+        """The same step with events around every partition-kernel launch."""
+        P, c, torch = self.P, self.case, self.torch
+        for l in range(self.layers):
+            P.kv_cache_write(self.nk[l], self.nv[l], self.K[l], self.V[l], self.slots)
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            P.paged_attention_decode_splitkv_partials(self.q[l], self.K[l], self.V[l], self.bt,
+                                                      self.cl, c.scale, c.gqa_factor, self.L,
+                                                      self.partition, self.ws)
+            e.record()
+            P.paged_attention_decode_splitkv_merge(self.out[l], self.cl, c.max_blocks, self.L,
+                                                   self.partition, self.ws)
+            ev.append((s, e))
+
+
+def time_steps(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps          # ms per step
+
+
+def kernel_average_ms(torch, wl, steps):
+    ev = []
+    for _ in range(steps):
+        wl.step_timed_kernels(ev)
+    torch.cuda.synchronize()
+    ms = [s.elapsed_time(e) for s, e in ev]
+    return sum(ms) / len(ms), len(ms)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the kernel source as it is now; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != source_digest():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, seconds):
+    """The oracle as it stands on layer 0 of the same workload, repeated until
+    about ``seconds`` of host time; reported in the metric's unit (GB/s)."""
+    import numpy as np
+    import oracle
+    c = wl.case
+    threads = 1
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([1] + [i.get("num_threads", 1) for i in threadpool_info()
+                             if i.get("user_api") == "blas"])
+    except Exception:
+        pass
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.paged_attention(c.query, c.key_cache, c.value_cache, c.block_tables,
+                               c.context_lens, c.scale, c.gqa_factor, "f16")
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 200:
+            break
+    return {"value": round(reps * wl.layer_bytes / el / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"layer 0 of the 32K workload (128 MiB of K/V), {reps} oracle runs in "
+                      f"{el:.1f} s; numpy float64 with {threads} BLAS thread(s), "
+                      f"host has {os.cpu_count()} logical CPUs"}
+
+
+# ----------------------------------------------------------------------------
+# The other four workloads (timing only: K/V drawn on the GPU, tables, lengths
+# and slots from the seeded generator).  Reported beside the headline.
+
+OTHER = {
+    # name: (seed, layers, split partition or 0 for the direct form)
+    "tiny": (1, 32, 0),
+    "llama8b_batch": (2, 8, 512),
+    "spec_verify": (4, 8, 512),
+    "k8v4": (5, 8, 512),
+}
+
+
+def other_workload(name, P, W, torch, steps, warmup):
+    seed, layers, part = OTHER[name]
+    lay, B, Q, Hq, Hkv, D, fmt = W.layout_of(name, seed)
+    dev = torch.device("cuda:0")
+    dt = torch.float16 if fmt == "f16" else torch.bfloat16
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed * 1000 + 7)
+    NB, G = lay.num_blocks, Hq // Hkv
+    scale = float(1.0 / D ** 0.5)
+    T = len(lay.slot_mapping)
+    bt = torch.from_numpy(lay.block_tables).to(dev)
+    cl = torch.from_numpy(lay.context_lens).to(dev)
+    slots = torch.from_numpy(lay.slot_mapping).to(dev)
+    mcl = int(lay.context_lens.max())
+    rnd = lambda *sh: torch.randn(sh, generator=gen, device=dev, dtype=dt)  # noqa: E731
+    q = [rnd(B, Q, Hq, D) for _ in range(layers)]
+    nk = [rnd(T, Hkv, D) for _ in range(layers)]
+    nv = [rnd(T, Hkv, D) for _ in range(layers)]
+    out = [torch.empty(B, Q, Hq, D, dtype=dt, device=dev) for _ in range(layers)]
+    ws = None
+    if part:
+        ws = torch.empty(P.splitkv_workspace_size(B, Q, Hq, D, mcl, part) // 4 + 4,
+                         dtype=torch.float32, device=dev)
+    sum_len = int(lay.context_lens.astype("int64").sum())
+    if name == "k8v4":
+        pools = []
+        all_slots = torch.arange(NB * 16, dtype=torch.int64, device=dev)
+        for _ in range(layers):
+            pool = dict(k=torch.empty(NB, 16, Hkv, D, dtype=torch.int8, device=dev),
+                        ks=torch.empty(NB, 16, Hkv, dtype=torch.float16, device=dev),
+                        v=torch.empty(NB, 16, Hkv, D // 2, dtype=torch.uint8, device=dev),
+                        vs=torch.empty(NB, 16, Hkv, D // 32, dtype=torch.float16, device=dev),
+                        vz=torch.empty(NB, 16, Hkv, D // 32, dtype=torch.float16, device=dev))
+            for c0 in range(0, NB * 16, 65536):
+                sl = all_slots[c0:c0 + 65536]
+                P.kv_cache_write_k8v4(rnd(len(sl), Hkv, D), rnd(len(sl), Hkv, D), pool["k"],
+                                      pool["ks"], pool["v"], pool["vs"], pool["vz"], sl)
+            pools.append(pool)
+        per_tok_head = D + 2 + D // 2 + 4 * (D // 32)
+
+        def step():
+            for l in range(layers):
+                p = pools[l]
+                P.kv_cache_write_k8v4(nk[l], nv[l], p["k"], p["ks"], p["v"], p["vs"], p["vz"], slots)
+                P.paged_attention_decode_splitkv_k8v4(out[l], q[l], p["k"], p["ks"], p["v"], p["vs"],
+                                                      p["vz"], bt, cl, scale, G, mcl, part, ws)
+    else:
+        K = [rnd(NB, 16, Hkv, D) for _ in range(layers)]
+        V = [rnd(NB, 16, Hkv, D) for _ in range(layers)]
+        per_tok_head = 4 * D
+
+        def step():
+            for l in range(layers):
+                P.kv_cache_write(nk[l], nv[l], K[l], V[l], slots)
+                if part:
+                    P.paged_attention_decode_splitkv(out[l], q[l], K[l], V[l], bt, cl, scale, G,
+                                                     mcl, part, ws)
+                else:
+                    P.paged_attention_decode(out[l], q[l], K[l], V[l], bt, cl, scale, G)
+    ms = time_steps(torch, step, steps, warmup)
+    layer_bytes = sum_len * Hkv * per_tok_head
+    us = ms * 1e3 / layers
+    return {"us_per_layer": round(us, 3), "kv_bytes_per_layer": layer_bytes,
+            "kv_stream_gbs": round(layer_bytes / (us * 1e-6) / 1e9, 2),
+            "pct_of_hbm_peak": round(100 * layer_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+            "decode_rows_per_s": round(B * Q / (ms * 1e-3), 1),
+            "layers": layers, "form": f"split-KV partition {part}" if part else "direct",
+            "writes_per_layer": T, "kv_format": "k8v4" if name == "k8v4" else fmt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    import paged_kv_cache_181_amd as P
+    from paged_kv_cache_181_amd import workloads as W
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU"}))
+        sys.exit(1)
+
+    log("building the 32K workload")
+    wl = Long32K(P, W, torch, args.layers, args.partition, args.seed)
+    log("timing steps")
+    ms = time_steps(torch, wl.step, args.steps, args.warmup)
+    gbs = wl.step_bytes / (ms * 1e-3) / 1e9
+    log(f"{ms:.3f} ms/step, {gbs:.1f} GB/s")
+    kern_ms, launches = kernel_average_ms(torch, wl, args.steps)
+    achieved = wl.layer_bytes / (kern_ms * 1e-3) / 1e9
+    log(f"partition kernel {kern_ms * 1e3:.2f} us avg over {launches} launches, {achieved:.1f} GB/s")
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": "long32k: single-user split-KV decode, batch 1, q_len 1, 32 query / 8 KV "
+                        "heads, head_dim 128, fp16 K/V, context 32768 (2048 blocks of 16, "
+                        "permuted pool), 32 layers, partition 512; per layer one token write "
+                        "+ partition kernel + LSE merge",
+            "batch": 1, "context": wl.L, "layers": args.layers, "partition_size": args.partition,
+            "kv_bytes_per_step": wl.step_bytes,
+        },
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "us_per_layer": round(ms * 1e3 / args.layers, 3),
+        "decode_tokens_per_s": round(1e3 / ms, 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "attn_partition_kernel<F16,F16,128>",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(),
+            "avg_launch_us": round(kern_ms * 1e3, 3),
+            "algorithmic_bytes_per_launch": wl.layer_bytes,
+        },
+    }
+    if not args.no_extra:
+        del wl.K, wl.V
+        torch.cuda.empty_cache()
+        result["other_workloads"] = {}
+        for name in ("tiny", "llama8b_batch", "spec_verify", "k8v4"):
+            log(f"timing {name}")
+            result["other_workloads"][name] = other_workload(name, P, W, torch, args.steps,
+                                                             args.warmup)
+            torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -145,6 +145,41 @@ int paged_attention_decode_splitkv(void* out, int out_dtype, const void* query,
                                    void* stream);
 
 /*
+ * The two halves of paged_attention_decode_splitkv, for callers that schedule
+ * or combine them themselves (e.g. to merge partials of several passes).
+ *
+ * paged_attention_decode_splitkv_partials launches only the partition kernel.
+ * Workspace layout (float32, rows = batch * q_len * num_q_heads in
+ * [b][i][h] order, P = ceil(max_context_len / partition_size)):
+ *   o[rows][P][head_dim]  unnormalised partial outputs  sum_j 2^(s_j - m) v_j
+ *   m[rows][P]            partition max of s_j = scale * q.k_j * log2(e)
+ *                         (-inf if the row sees no position in the partition)
+ *   l[rows][P]            sum_j 2^(s_j - m)
+ * Partition p covers positions [p * partition_size, (p+1) * partition_size),
+ * the last one runs to the end of the sequence; partitions that start at or
+ * past a sequence's length are not written.
+ *
+ * paged_attention_decode_splitkv_merge reads those partials (only partitions
+ * that start before each sequence's clamped length) and writes
+ * out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p with M = max_p m_p
+ * (zeros where no partition saw a position).
+ */
+int paged_attention_decode_splitkv_partials(const void* query, const void* key_cache,
+                                            const void* value_cache, int kv_dtype,
+                                            const int32_t* block_tables, int max_blocks_per_seq,
+                                            const int32_t* context_lens, int batch, int q_len,
+                                            int num_q_heads, int gqa_factor, int head_dim,
+                                            int block_size, int64_t num_blocks, float scale,
+                                            int max_context_len, int partition_size,
+                                            void* workspace, size_t workspace_bytes, void* stream);
+
+int paged_attention_decode_splitkv_merge(void* out, int out_dtype, const int32_t* context_lens,
+                                         int max_blocks_per_seq, int batch, int q_len,
+                                         int num_q_heads, int head_dim, int max_context_len,
+                                         int partition_size, const void* workspace,
+                                         size_t workspace_bytes, void* stream);
+
+/*
  * kv_cache_write_k8v4 — quantize-on-write into a K8/V4 cache.
  *   key, value: [num_tokens, num_kv_heads, head_dim] of in_dtype (f16 or bf16)
  *   k_cache int8   [num_blocks, block_size, num_kv_heads, head_dim]
@@ -188,6 +223,16 @@ int paged_attention_decode_splitkv_k8v4(void* out, int out_dtype, const void* qu
                                         int head_dim, int block_size, int64_t num_blocks,
                                         float scale, int max_context_len, int partition_size,
                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Partition-kernel half of paged_attention_decode_splitkv_k8v4 (merge with
+ * paged_attention_decode_splitkv_merge). */
+int paged_attention_decode_splitkv_k8v4_partials(
+    const void* query, int q_dtype, const int8_t* k_cache, const void* k_scale,
+    const uint8_t* v_cache, const void* v_scale, const void* v_zero, const int32_t* block_tables,
+    int max_blocks_per_seq, const int32_t* context_lens, int batch, int q_len, int num_q_heads,
+    int gqa_factor, int head_dim, int block_size, int64_t num_blocks, float scale,
+    int max_context_len, int partition_size, void* workspace, size_t workspace_bytes,
+    void* stream);
 
 /*
  * Cache bytes one token occupies over all layers (host-only arithmetic).

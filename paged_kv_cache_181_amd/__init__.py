@@ -15,6 +15,8 @@ _EXPORTS = (
     "kv_cache_write_k8v4", "last_error", "lib", "paged_attention_decode",
     "paged_attention_decode_k8v4", "paged_attention_decode_splitkv",
     "paged_attention_decode_splitkv_k8v4", "splitkv_workspace_size", "version",
+    "paged_attention_decode_splitkv_partials", "paged_attention_decode_splitkv_k8v4_partials",
+    "paged_attention_decode_splitkv_merge",
 )
 
 __all__ = list(_EXPORTS)

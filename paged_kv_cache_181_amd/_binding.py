@@ -58,6 +58,10 @@ SIGNATURES = {
     "paged_attention_decode_k8v4": (_ATTN_K8V4 + [_p], _i),
     "paged_attention_decode_splitkv_k8v4": (_ATTN_K8V4 + [_i, _i, _p, _sz, _p], _i),
     "kv_cache_bytes_per_token": ([_i, _i, _i, _i, ctypes.POINTER(_i64)], _i),
+    "paged_attention_decode_splitkv_partials": (_ATTN[2:] + [_i, _i, _p, _sz, _p], _i),
+    "paged_attention_decode_splitkv_k8v4_partials": (_ATTN_K8V4[2:] + [_i, _i, _p, _sz, _p], _i),
+    "paged_attention_decode_splitkv_merge": ([_p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p, _sz, _p],
+                                             _i),
 }
 for _name, (_args, _res) in SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -251,3 +255,49 @@ def paged_attention_decode_splitkv_k8v4(out, query, k_cache, k_scale, v_cache, v
         _ptr(v_cache), _ptr(v_scale), _ptr(v_zero), _ptr(block_tables), block_tables.shape[1],
         _ptr(context_lens), B, Q, Hq, gqa_factor, D, bs, nb, float(scale), int(max_context_len),
         int(partition_size), _ptr(workspace), nbytes, _stream(dev)))
+
+
+def paged_attention_decode_splitkv_partials(query, key_cache, value_cache, block_tables,
+                                            context_lens, scale, gqa_factor, max_context_len,
+                                            partition_size, workspace):
+    """Partition kernel only: per-partition (o, m, l) into ``workspace``."""
+    dev = _dev(query, key_cache, value_cache, block_tables, context_lens, workspace)
+    B, Q, Hq, D = _attn_common(query, query, block_tables, context_lens, gqa_factor)
+    _expect(key_cache.shape == value_cache.shape and key_cache.shape[2:] == (Hq // gqa_factor, D),
+            "caches must be [NB, 16, Hq/G, D]")
+    _expect(query.dtype == key_cache.dtype == value_cache.dtype, "query/cache dtype mismatch")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.paged_attention_decode_splitkv_partials(
+        _ptr(query), _ptr(key_cache), _ptr(value_cache), _dtype_code(key_cache),
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, Q, Hq, gqa_factor, D,
+        key_cache.shape[1], key_cache.shape[0], float(scale), int(max_context_len),
+        int(partition_size), _ptr(workspace), nbytes, _stream(dev)))
+
+
+def paged_attention_decode_splitkv_k8v4_partials(query, k_cache, k_scale, v_cache, v_scale, v_zero,
+                                                 block_tables, context_lens, scale, gqa_factor,
+                                                 max_context_len, partition_size, workspace):
+    dev = _dev(query, k_cache, k_scale, v_cache, v_scale, v_zero, block_tables, context_lens,
+               workspace)
+    B, Q, Hq, D = _attn_common(query, query, block_tables, context_lens, gqa_factor)
+    nb, bs = _k8v4_check(query, gqa_factor, k_cache, k_scale, v_cache, v_scale, v_zero)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.paged_attention_decode_splitkv_k8v4_partials(
+        _ptr(query), _dtype_code(query), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache),
+        _ptr(v_scale), _ptr(v_zero), _ptr(block_tables), block_tables.shape[1],
+        _ptr(context_lens), B, Q, Hq, gqa_factor, D, bs, nb, float(scale), int(max_context_len),
+        int(partition_size), _ptr(workspace), nbytes, _stream(dev)))
+
+
+def paged_attention_decode_splitkv_merge(out, context_lens, max_blocks_per_seq, max_context_len,
+                                         partition_size, workspace):
+    """Log-sum-exp merge of the partials in ``workspace`` into ``out`` [B, Q, Hq, D]."""
+    torch = _torch()
+    dev = _dev(out, context_lens, workspace)
+    _expect(out.dim() == 4, "out must be [B, Q, Hq, D]")
+    B, Q, Hq, D = out.shape
+    _expect(context_lens.dtype == torch.int32 and context_lens.shape == (B,), "context_lens int32 [B]")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.paged_attention_decode_splitkv_merge(
+        _ptr(out), _dtype_code(out), _ptr(context_lens), int(max_blocks_per_seq), B, Q, Hq, D,
+        int(max_context_len), int(partition_size), _ptr(workspace), nbytes, _stream(dev)))

@@ -51,7 +51,7 @@ int check_attention(void* out, int out_dtype, const void* query, const void* k_c
                     const void* v_cache, const int32_t* block_tables, int max_blocks,
                     const int32_t* context_lens, int batch, int q_len, int num_q_heads,
                     int gqa_factor, int head_dim, int block_size, int64_t num_blocks, float scale,
-                    pkv::AttnArgs& a) {
+                    pkv::AttnArgs& a, bool need_out = true) {
   if (batch < 0 || q_len <= 0 || num_q_heads <= 0 || gqa_factor <= 0 || max_blocks < 0)
     return fail(PKV_ERR_SHAPE, "batch >= 0, q_len > 0, num_q_heads > 0, gqa_factor > 0, "
                                "max_blocks_per_seq >= 0 required");
@@ -64,12 +64,12 @@ int check_attention(void* out, int out_dtype, const void* query, const void* k_c
   if ((int64_t)gqa_factor * q_len > 16)
     return fail(PKV_ERR_UNSUPPORTED, "gqa_factor * q_len must be <= 16 (got %d)",
                 gqa_factor * q_len);
-  if (out_dtype != PKV_F16 && out_dtype != PKV_BF16 && out_dtype != PKV_F32)
+  if (need_out && out_dtype != PKV_F16 && out_dtype != PKV_BF16 && out_dtype != PKV_F32)
     return fail(PKV_ERR_UNSUPPORTED, "out_dtype must be PKV_F16, PKV_BF16 or PKV_F32");
   if (!std::isfinite(scale)) return fail(PKV_ERR_SHAPE, "scale must be finite");
   if (batch > 65535 || hkv > 65535) return fail(PKV_ERR_UNSUPPORTED, "batch or KV heads too large");
   if (batch == 0) return PKV_OK;
-  if (!out || !query || !k_cache || !v_cache || !block_tables || !context_lens)
+  if ((need_out && !out) || !query || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PKV_ERR_NULL, "a required pointer is NULL");
   if (!aligned16(query) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PKV_ERR_ALIGN, "query and caches must be 16-byte aligned");
@@ -314,6 +314,100 @@ int paged_attention_decode_splitkv_k8v4(void* out, int out_dtype, const void* qu
   return launch_result(pkv::launch_attention(a, PKV_FMT_K8V4, q_dtype, head_dim,
                                              (hipStream_t)stream),
                        "paged_attention_decode_splitkv_k8v4");
+}
+
+int paged_attention_decode_splitkv_partials(const void* query, const void* key_cache,
+                                            const void* value_cache, int kv_dtype,
+                                            const int32_t* block_tables, int max_blocks_per_seq,
+                                            const int32_t* context_lens, int batch, int q_len,
+                                            int num_q_heads, int gqa_factor, int head_dim,
+                                            int block_size, int64_t num_blocks, float scale,
+                                            int max_context_len, int partition_size,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* stream) {
+  if (kv_dtype != PKV_F16 && kv_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "kv_dtype must be PKV_F16 or PKV_BF16");
+  pkv::AttnArgs a{};
+  int rc = check_attention(nullptr, PKV_F32, query, key_cache, value_cache, block_tables,
+                           max_blocks_per_seq, context_lens, batch, q_len, num_q_heads, gqa_factor,
+                           head_dim, block_size, num_blocks, scale, a, false);
+  if (rc) return rc;
+  if (batch == 0) return ok();
+  rc = setup_split(a, head_dim, max_context_len, partition_size, workspace, workspace_bytes);
+  if (rc) return rc;
+  return launch_result(pkv::launch_attention(a, kv_dtype, kv_dtype, head_dim, (hipStream_t)stream,
+                                             pkv::STAGE_PARTIALS),
+                       "paged_attention_decode_splitkv_partials");
+}
+
+int paged_attention_decode_splitkv_k8v4_partials(
+    const void* query, int q_dtype, const int8_t* k_cache, const void* k_scale,
+    const uint8_t* v_cache, const void* v_scale, const void* v_zero, const int32_t* block_tables,
+    int max_blocks_per_seq, const int32_t* context_lens, int batch, int q_len, int num_q_heads,
+    int gqa_factor, int head_dim, int block_size, int64_t num_blocks, float scale,
+    int max_context_len, int partition_size, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  if (q_dtype != PKV_F16 && q_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "q_dtype must be PKV_F16 or PKV_BF16");
+  pkv::AttnArgs a{};
+  int rc = check_attention(nullptr, PKV_F32, query, k_cache, v_cache, block_tables,
+                           max_blocks_per_seq, context_lens, batch, q_len, num_q_heads, gqa_factor,
+                           head_dim, block_size, num_blocks, scale, a, false);
+  if (rc) return rc;
+  if (batch == 0) return ok();
+  rc = check_k8v4_pointers(k_scale, v_scale, v_zero);
+  if (rc) return rc;
+  rc = setup_split(a, head_dim, max_context_len, partition_size, workspace, workspace_bytes);
+  if (rc) return rc;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.v_zero = v_zero;
+  return launch_result(pkv::launch_attention(a, PKV_FMT_K8V4, q_dtype, head_dim,
+                                             (hipStream_t)stream, pkv::STAGE_PARTIALS),
+                       "paged_attention_decode_splitkv_k8v4_partials");
+}
+
+int paged_attention_decode_splitkv_merge(void* out, int out_dtype, const int32_t* context_lens,
+                                         int max_blocks_per_seq, int batch, int q_len,
+                                         int num_q_heads, int head_dim, int max_context_len,
+                                         int partition_size, const void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  if (batch < 0 || q_len <= 0 || num_q_heads <= 0 || max_blocks_per_seq < 0)
+    return fail(PKV_ERR_SHAPE, "batch >= 0, q_len > 0, num_q_heads > 0 required");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  if (out_dtype != PKV_F16 && out_dtype != PKV_BF16 && out_dtype != PKV_F32)
+    return fail(PKV_ERR_UNSUPPORTED, "out_dtype must be PKV_F16, PKV_BF16 or PKV_F32");
+  if (batch > 65535) return fail(PKV_ERR_UNSUPPORTED, "batch too large");
+  int64_t parts = 0;
+  size_t need = 0;
+  int rc = split_geometry(batch, q_len, num_q_heads, head_dim, max_context_len, partition_size,
+                          parts, need);
+  if (rc) return rc;
+  if (batch == 0) return ok();
+  if (!out || !context_lens) return fail(PKV_ERR_NULL, "a required pointer is NULL");
+  if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(PKV_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed",
+                workspace_bytes, need);
+  pkv::AttnArgs a{};
+  a.out = out;
+  a.out_dtype = out_dtype;
+  a.context_lens = context_lens;
+  a.max_blocks = max_blocks_per_seq;
+  a.batch = batch;
+  a.q_len = q_len;
+  a.num_q_heads = num_q_heads;
+  const int64_t rows = (int64_t)batch * q_len * num_q_heads;
+  a.num_parts = (int)parts;
+  a.part_blocks = partition_size / 16;
+  a.ws_o = (float*)workspace;
+  a.ws_m = a.ws_o + rows * parts * head_dim;
+  a.ws_l = a.ws_m + rows * parts;
+  return launch_result(pkv::launch_attention(a, PKV_FMT_F16, PKV_F16, head_dim,
+                                             (hipStream_t)stream, pkv::STAGE_MERGE),
+                       "paged_attention_decode_splitkv_merge");
 }
 
 }  // extern "C"

@@ -461,30 +461,39 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
   }
 }
 
-template <Fmt KV, Fmt QT, int D>
-static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream) {
-  const dim3 grid((unsigned)a.num_parts, (unsigned)a.num_kv_heads, (unsigned)a.batch);
-  hipLaunchKernelGGL((attn_partition_kernel<KV, QT, D>), grid, dim3(NW * kWave), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.ws_o == nullptr) return e;
+template <int D>
+static hipError_t launch_merge(const AttnArgs& a, hipStream_t stream) {
   const unsigned rows = (unsigned)((int64_t)a.batch * a.q_len * a.num_q_heads);
   hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(rows), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
+template <Fmt KV, Fmt QT, int D>
+static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream, int stage) {
+  if (stage != STAGE_MERGE) {
+    const dim3 grid((unsigned)a.num_parts, (unsigned)a.num_kv_heads, (unsigned)a.batch);
+    hipLaunchKernelGGL((attn_partition_kernel<KV, QT, D>), grid, dim3(NW * kWave), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.ws_o == nullptr || stage == STAGE_PARTIALS) return e;
+  }
+  return launch_merge<D>(a, stream);
+}
+
 template <int D>
-static hipError_t launch_d(const AttnArgs& a, int kv_fmt, int q_fmt, hipStream_t stream) {
-  if (kv_fmt == (int)Fmt::F16) return launch_typed<Fmt::F16, Fmt::F16, D>(a, stream);
-  if (kv_fmt == (int)Fmt::BF16) return launch_typed<Fmt::BF16, Fmt::BF16, D>(a, stream);
-  if (q_fmt == (int)Fmt::F16) return launch_typed<Fmt::K8V4, Fmt::F16, D>(a, stream);
-  return launch_typed<Fmt::K8V4, Fmt::BF16, D>(a, stream);
+static hipError_t launch_d(const AttnArgs& a, int kv_fmt, int q_fmt, hipStream_t stream,
+                           int stage) {
+  if (stage == STAGE_MERGE) return launch_merge<D>(a, stream);
+  if (kv_fmt == (int)Fmt::F16) return launch_typed<Fmt::F16, Fmt::F16, D>(a, stream, stage);
+  if (kv_fmt == (int)Fmt::BF16) return launch_typed<Fmt::BF16, Fmt::BF16, D>(a, stream, stage);
+  if (q_fmt == (int)Fmt::F16) return launch_typed<Fmt::K8V4, Fmt::F16, D>(a, stream, stage);
+  return launch_typed<Fmt::K8V4, Fmt::BF16, D>(a, stream, stage);
 }
 
 hipError_t launch_attention(const AttnArgs& a, int kv_fmt, int q_fmt, int head_dim,
-                            hipStream_t stream) {
+                            hipStream_t stream, int stage) {
   if (a.batch == 0) return hipSuccess;
-  return head_dim == 64 ? launch_d<64>(a, kv_fmt, q_fmt, stream)
-                        : launch_d<128>(a, kv_fmt, q_fmt, stream);
+  return head_dim == 64 ? launch_d<64>(a, kv_fmt, q_fmt, stream, stage)
+                        : launch_d<128>(a, kv_fmt, q_fmt, stream, stage);
 }
 
 }  // namespace pkv

@@ -39,7 +39,10 @@ struct AttnArgs {
 };
 
 // kv_fmt: 0 f16, 1 bf16, 3 k8v4; q_fmt: 0 f16, 1 bf16 (must equal kv_fmt unless k8v4).
+// stage: STAGE_ALL launches the partition kernel and, for the split form, the
+// merge; STAGE_PARTIALS only the partition kernel; STAGE_MERGE only the merge.
+enum { STAGE_ALL = 0, STAGE_PARTIALS = 1, STAGE_MERGE = 2 };
 hipError_t launch_attention(const AttnArgs& a, int kv_fmt, int q_fmt, int head_dim,
-                            hipStream_t stream);
+                            hipStream_t stream, int stage = STAGE_ALL);
 
 }  // namespace pkv

@@ -122,38 +122,56 @@ def fill_pool(rng, tables, blocks_needed, num_blocks, num_kv_heads, head_dim, fm
     return kc, vc
 
 
-def make_case(name: str, seed: int, *, batch: int, q_len: int, num_q_heads: int,
-              num_kv_heads: int, head_dim: int, fmt: str, lengths,
-              num_blocks: Optional[int] = None, spare_blocks: int = 0,
-              extra_positions: int = 0, accept: bool = False) -> PagedCase:
-    """General builder.  ``lengths`` is an int array, or a callable
-    ``rng -> int array`` drawn after the table permutation size is known.
+@dataclass
+class Layout:
+    """Lengths, block tables and this step's slots, without any K/V values."""
+    context_lens: np.ndarray
+    block_tables: np.ndarray
+    num_blocks: int
+    slot_mapping: np.ndarray
+    blocks_needed: np.ndarray
 
-    Tables cover ``length + extra_positions`` positions per row so that a
-    follow-up write (after a verify step) always has a block.
-    """
-    rng = rng_for(seed)
+
+def make_layout(rng, *, batch: int, q_len: int, lengths, num_blocks: Optional[int] = None,
+                spare_blocks: int = 0, extra_positions: int = 0) -> Layout:
+    """Draw the lengths (if a callable) and the table permutation.  Tables
+    cover ``length + extra_positions`` positions per row so that a follow-up
+    write (after a verify step) always has a block."""
     lengths_arr = np.asarray(lengths(rng) if callable(lengths) else lengths, dtype=np.int64)
     if lengths_arr.shape != (batch,):
         raise ValueError("lengths must have one entry per row")
     need = (lengths_arr + extra_positions + BLOCK_SIZE - 1) // BLOCK_SIZE
     nb = int(num_blocks if num_blocks is not None else need.sum() + spare_blocks)
     tables = build_tables(rng, need, nb)
-    kc, vc = fill_pool(rng, tables, need, nb, num_kv_heads, head_dim, fmt)
-    query = normal_bits(rng, (batch, q_len, num_q_heads, head_dim), fmt)
     # this step's tokens: positions L-q_len .. L-1 of every row
     slots = [slot_of(tables, b, int(lengths_arr[b]) - q_len + i)
              if int(lengths_arr[b]) - q_len + i >= 0 else -1
              for b in range(batch) for i in range(q_len)]
-    new_key = normal_bits(rng, (len(slots), num_kv_heads, head_dim), fmt)
-    new_value = normal_bits(rng, (len(slots), num_kv_heads, head_dim), fmt)
+    return Layout(lengths_arr.astype(np.int32), tables, nb, np.asarray(slots, dtype=np.int64), need)
+
+
+def make_case(name: str, seed: int, *, batch: int, q_len: int, num_q_heads: int,
+              num_kv_heads: int, head_dim: int, fmt: str, lengths,
+              num_blocks: Optional[int] = None, spare_blocks: int = 0,
+              extra_positions: int = 0, accept: bool = False) -> PagedCase:
+    """General builder.  ``lengths`` is an int array, or a callable
+    ``rng -> int array``."""
+    rng = rng_for(seed)
+    lay = make_layout(rng, batch=batch, q_len=q_len, lengths=lengths, num_blocks=num_blocks,
+                      spare_blocks=spare_blocks, extra_positions=extra_positions)
+    kc, vc = fill_pool(rng, lay.block_tables, lay.blocks_needed, lay.num_blocks, num_kv_heads,
+                       head_dim, fmt)
+    query = normal_bits(rng, (batch, q_len, num_q_heads, head_dim), fmt)
+    t = len(lay.slot_mapping)
+    new_key = normal_bits(rng, (t, num_kv_heads, head_dim), fmt)
+    new_value = normal_bits(rng, (t, num_kv_heads, head_dim), fmt)
     accepted = rng.integers(0, q_len + 1, size=batch).astype(np.int32) if accept else None
     return PagedCase(
         name=name, batch=batch, q_len=q_len, num_q_heads=num_q_heads,
-        num_kv_heads=num_kv_heads, head_dim=head_dim, fmt=fmt, num_blocks=nb,
-        context_lens=lengths_arr.astype(np.int32), block_tables=tables,
+        num_kv_heads=num_kv_heads, head_dim=head_dim, fmt=fmt, num_blocks=lay.num_blocks,
+        context_lens=lay.context_lens, block_tables=lay.block_tables,
         key_cache=kc, value_cache=vc, query=query, new_key=new_key, new_value=new_value,
-        slot_mapping=np.asarray(slots, dtype=np.int64),
+        slot_mapping=lay.slot_mapping,
         scale=float(np.float32(1.0 / np.sqrt(head_dim))), accepted=accepted)
 
 
@@ -205,6 +223,28 @@ def k8v4(seed: int = 5, batch: int = 16, length: int = 8192) -> PagedCase:
     nb = batch * ((length + BLOCK_SIZE - 1) // BLOCK_SIZE)
     return make_case("k8v4", seed, batch=batch, q_len=1, num_q_heads=32, num_kv_heads=8,
                      head_dim=128, fmt="f16", lengths=[length] * batch, num_blocks=nb)
+
+
+def layout_of(name: str, seed: int) -> tuple:
+    """(Layout, batch, q_len, Hq, Hkv, D, fmt) of a named workload, drawing only
+    the lengths and tables (same draws as the full builder up to that point)."""
+    rng = rng_for(seed)
+    if name == "tiny":
+        return make_layout(rng, batch=1, q_len=1, lengths=[256], num_blocks=64), 1, 1, 8, 2, 64, "f16"
+    if name == "llama8b_batch":
+        return (make_layout(rng, batch=32, q_len=1, lengths=lambda r: r.integers(512, 4097, size=32),
+                            num_blocks=16384), 32, 1, 32, 8, 128, "bf16")
+    if name == "long32k":
+        return make_layout(rng, batch=1, q_len=1, lengths=[32768], num_blocks=2048), 1, 1, 32, 8, 128, "f16"
+    if name == "spec_verify":
+        def lengths(r):
+            return np.round(np.exp(r.uniform(np.log(256), np.log(16384), size=64))).astype(np.int64)
+        return (make_layout(rng, batch=64, q_len=4, lengths=lengths, spare_blocks=64,
+                            extra_positions=1), 64, 4, 32, 8, 128, "bf16")
+    if name == "k8v4":
+        return (make_layout(rng, batch=16, q_len=1, lengths=[8192] * 16, num_blocks=8192),
+                16, 1, 32, 8, 128, "f16")
+    raise KeyError(name)
 
 
 WORKLOADS = {
