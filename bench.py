@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip the other four workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (scale for rocprofv3 byte counters)")
     return ap.parse_args()
 
 
@@ -110,20 +112,26 @@ class Long32K:
                                              self.cl, c.scale, c.gqa_factor, self.L,
                                              self.partition, self.ws)
 
-    def step_timed_kernels(self, ev):
-        """The same step with events around every partition-kernel launch."""
+    def step_timed_kernels(self):
+        """The same work as a step, reordered so that the 32 partition-kernel
+        launches run back to back between two events: all writes first, then
+        the partition kernels (one workspace per layer), then the merges."""
         P, c, torch = self.P, self.case, self.torch
+        if not hasattr(self, "wss"):
+            self.wss = [torch.empty_like(self.ws) for _ in range(self.layers)]
         for l in range(self.layers):
             P.kv_cache_write(self.nk[l], self.nv[l], self.K[l], self.V[l], self.slots)
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for l in range(self.layers):
             P.paged_attention_decode_splitkv_partials(self.q[l], self.K[l], self.V[l], self.bt,
                                                       self.cl, c.scale, c.gqa_factor, self.L,
-                                                      self.partition, self.ws)
-            e.record()
+                                                      self.partition, self.wss[l])
+        e.record()
+        for l in range(self.layers):
             P.paged_attention_decode_splitkv_merge(self.out[l], self.cl, c.max_blocks, self.L,
-                                                   self.partition, self.ws)
-            ev.append((s, e))
+                                                   self.partition, self.wss[l])
+        return s, e
 
 
 def time_steps(torch, fn, steps, warmup):
@@ -140,12 +148,16 @@ def time_steps(torch, fn, steps, warmup):
 
 
 def kernel_average_ms(torch, wl, steps):
-    ev = []
+    """Average partition-kernel duration from HIP events on its launch stream:
+    one event pair around the 32 back-to-back partition launches of a step (the
+    merges follow after the closing event), averaged over ``steps`` steps."""
+    total, n = 0.0, 0
     for _ in range(steps):
-        wl.step_timed_kernels(ev)
-    torch.cuda.synchronize()
-    ms = [s.elapsed_time(e) for s, e in ev]
-    return sum(ms) / len(ms), len(ms)
+        ev = wl.step_timed_kernels()
+        torch.cuda.synchronize()
+        total += ev[0].elapsed_time(ev[1])
+        n += wl.layers
+    return total / n, n
 
 
 def source_digest():
@@ -280,6 +292,21 @@ def other_workload(name, P, W, torch, steps, warmup):
             "writes_per_layer": T, "kv_format": "k8v4" if name == "k8v4" else fmt}
 
 
+def copy_calibration(torch):
+    """A plain device copy of known size: 1 GiB read + 1 GiB written per launch.
+    rocprofv3's FETCH_SIZE / WRITE_SIZE for these launches give the scale
+    from counter units to bytes for the same counters on our kernels."""
+    n = 1 << 30
+    src = torch.empty(n // 2, dtype=torch.float16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n,
+                      "launches": 5}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -291,6 +318,9 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU"}))
         sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
 
     log("building the 32K workload")
     wl = Long32K(P, W, torch, args.layers, args.partition, args.seed)

@@ -138,7 +138,8 @@ __global__ __launch_bounds__(NW * kWave) void attn_partition_kernel(const AttnAr
   __shared__ __align__(16) unsigned char smem[SM::BYTES];
   __shared__ float mm_s[NW][16], ml_s[NW][16];
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int rho = lane & 15, qd = lane >> 4;
   const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int Q = a.q_len, G = a.gqa, GQ = G * Q, Hq = a.num_q_heads;
@@ -180,8 +181,14 @@ __global__ __launch_bounds__(NW * kWave) void attn_partition_kernel(const AttnAr
   const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
   const float sl2 = a.scale_log2;
 
-  auto fetch = [&](int i, BlockRegs<KV, D>& br) -> bool {
-    int pb = __builtin_amdgcn_readfirstlane(bt[i]);
+  // This wave's blocks are bb + w + NW*k, k = 0 .. nmine-1.  Their table
+  // entries are read 64 at a time into one VGPR (lane j holds entry j of the
+  // chunk) and picked out with readlane, so no table load sits between the
+  // K/V loads of consecutive blocks.
+  const int nmine = be > bb + w ? (be - bb - w + NW - 1) / NW : 0;
+  int tblv = 0;
+  auto fetch = [&](int j, BlockRegs<KV, D>& br) -> bool {
+    const int pb = __builtin_amdgcn_readlane(tblv, j);
     const bool ok = pb >= 0 && (int64_t)pb < a.num_blocks;
     load_block<KV, D>(a, ok ? pb : 0, g, rho, qd, br);
     return ok;
@@ -332,21 +339,30 @@ __global__ __launch_bounds__(NW * kWave) void attn_partition_kernel(const AttnAr
     wave_lds_fence();
   };
 
-  // ---- block loop, two register sets so the next block's loads are in flight
-  {
-    BlockRegs<KV, D> ra, rb;
-    int i = bb + w;
-    bool oka = false, okb = false;
-    if (i < be) oka = fetch(i, ra);
-    while (i < be) {
-      const int i2 = i + NW;
-      if (i2 < be) okb = fetch(i2, rb);
-      process(i, oka, ra);
-      if (i2 >= be) break;
-      const int i3 = i2 + NW;
-      if (i3 < be) oka = fetch(i3, ra);
-      process(i2, okb, rb);
-      i = i3;
+  // ---- block loop, in chunks of 64 of this wave's blocks.  Two register
+  // sets: in the steady state the next block's loads are always issued before
+  // the current block is consumed, with no branch between them, so the wait
+  // before each block covers only that block's loads.
+  for (int c0 = 0; c0 < nmine; c0 += 64) {
+    const int cnt = min(64, nmine - c0);
+    tblv = lane < cnt ? bt[bb + w + NW * (c0 + lane)] : 0;
+    const int i0 = bb + w + NW * c0;
+    BlockRegs<KV, D> r0, r1;
+    bool ok0 = fetch(0, r0), ok1 = false;
+    int k = 0;
+    for (int pr = (cnt - 1) >> 1; pr > 0; --pr) {     // branch-free pairs of blocks
+      ok1 = fetch(k + 1, r1);
+      process(i0 + NW * k, ok0, r0);
+      ok0 = fetch(k + 2, r0);
+      process(i0 + NW * (k + 1), ok1, r1);
+      k += 2;
+    }
+    if (k + 1 < cnt) {                                // two blocks left
+      ok1 = fetch(k + 1, r1);
+      process(i0 + NW * k, ok0, r0);
+      process(i0 + NW * (k + 1), ok1, r1);
+    } else {                                          // one block left
+      process(i0 + NW * k, ok0, r0);
     }
   }
 

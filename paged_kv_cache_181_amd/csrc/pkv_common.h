@@ -111,10 +111,11 @@ __device__ __forceinline__ float wave_xor(float v, int mask) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Orders this wave's LDS accesses around a cross-lane exchange through LDS.
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-}
+// Keeps the compiler from reordering this wave's LDS accesses across a
+// cross-lane exchange through LDS.  The hardware executes the LDS instructions
+// of one wavefront in issue order, so no wait is needed, and none is emitted
+// (a memory fence here would also wait for the global loads in flight).
+__device__ __forceinline__ void wave_lds_fence() { asm volatile("" ::: "memory"); }
 
 __device__ __forceinline__ void store_out(void* out, OutT t, int64_t idx, float v) {
   if (t == OutT::F32) {
