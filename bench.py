@@ -4,16 +4,16 @@
 Headline workload: single-user long-context split-KV decode.  One step is one
 decoded token through 32 layers; per layer it writes the new token's K/V into
 that layer's block-paged cache (kv_cache_write) and runs split-KV paged
-attention over the 32768-token context (partition 512: partition kernel + log-
-sum-exp merge).  Batch 1, q_len 1, 32 query / 8 KV heads, head_dim 128, fp16,
+attention over the 32768-token context (partition 512: partition kernel, then
+a log-sum-exp merge kernel).  Batch 1, q_len 1, 32 query / 8 KV heads, head_dim 128, fp16,
 2048 blocks of 16 per layer in a randomly permuted pool, one block table shared
 by the layers.  32 distinct layer caches (4 GiB) keep the working set far
 beyond the 256 MB Infinity Cache.
 
 value = KV bytes streamed per step (32 x 128 MiB) / step time, with all inputs
 resident in HBM.  The dominant kernel's roofline entry uses HIP events around
-each partition-kernel launch on the launch stream, in a second pass of the same
-steps (the headline pass carries no per-launch events).
+32 back-to-back launches of the partition kernel on its launch stream, in a
+second pass of the same work (the headline pass carries no extra events).
 
 python bench.py [--steps K] [--warmup W] [--no-extra] [--no-cpu-baseline]
 """
@@ -99,7 +99,7 @@ class Long32K:
         self.out = [torch.empty(case.query.shape, dtype=torch.float16, device=dev)
                     for _ in range(layers)]
         nbytes = P.splitkv_workspace_size(1, 1, self.hq, self.d, self.L, partition)
-        self.ws = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+        self.ws = torch.zeros(nbytes // 4, dtype=torch.float32, device=dev)
         # algorithmic KV bytes one layer must read: K and V rows of every position
         self.layer_bytes = self.L * self.hkv * self.d * 2 * 2
         self.step_bytes = self.layer_bytes * layers
@@ -118,7 +118,7 @@ class Long32K:
         the partition kernels (one workspace per layer), then the merges."""
         P, c, torch = self.P, self.case, self.torch
         if not hasattr(self, "wss"):
-            self.wss = [torch.empty_like(self.ws) for _ in range(self.layers)]
+            self.wss = [torch.zeros_like(self.ws) for _ in range(self.layers)]
         for l in range(self.layers):
             P.kv_cache_write(self.nk[l], self.nv[l], self.K[l], self.V[l], self.slots)
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -129,8 +129,7 @@ class Long32K:
                                                       self.partition, self.wss[l])
         e.record()
         for l in range(self.layers):
-            P.paged_attention_decode_splitkv_merge(self.out[l], self.cl, c.max_blocks, self.L,
-                                                   self.partition, self.wss[l])
+            P.paged_attention_decode_splitkv_merge(self.out[l], self.L, self.partition, self.wss[l])
         return s, e
 
 
@@ -243,7 +242,7 @@ def other_workload(name, P, W, torch, steps, warmup):
     out = [torch.empty(B, Q, Hq, D, dtype=dt, device=dev) for _ in range(layers)]
     ws = None
     if part:
-        ws = torch.empty(P.splitkv_workspace_size(B, Q, Hq, D, mcl, part) // 4 + 4,
+        ws = torch.zeros(P.splitkv_workspace_size(B, Q, Hq, D, mcl, part) // 4 + 4,
                          dtype=torch.float32, device=dev)
     sum_len = int(lay.context_lens.astype("int64").sum())
     if name == "k8v4":
@@ -349,7 +348,7 @@ def main():
             "workload": "long32k: single-user split-KV decode, batch 1, q_len 1, 32 query / 8 KV "
                         "heads, head_dim 128, fp16 K/V, context 32768 (2048 blocks of 16, "
                         "permuted pool), 32 layers, partition 512; per layer one token write "
-                        "+ partition kernel + LSE merge",
+                        "+ partition kernel + LSE merge kernel",
             "batch": 1, "context": wl.L, "layers": args.layers, "partition_size": args.partition,
             "kv_bytes_per_step": wl.step_bytes,
         },
@@ -358,7 +357,7 @@ def main():
         "decode_tokens_per_s": round(1e3 / ms, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "attn_partition_kernel<F16,F16,128>",
+            "kernel": "attn_partition_kernel<F16,F16,128,4>",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

@@ -130,10 +130,11 @@ int paged_attention_decode_splitkv_workspace_size(int batch, int q_len, int num_
 /*
  * paged_attention_decode_splitkv — partition kernel over
  * (partition, KV head, sequence) writing per-partition (o, max, sum) to
- * `workspace`, then a log-sum-exp merge kernel writing `out`.  Same arguments
- * and result as paged_attention_decode (up to fp32 summation order).  The
- * workspace contents on entry do not matter; two calls that overlap in time
- * must not share a workspace.
+ * `workspace` (partitions that start past a sequence's end are marked empty),
+ * then a log-sum-exp merge kernel writing `out`.  Same arguments and result as
+ * paged_attention_decode (up to fp32 summation order).  The workspace
+ * contents on entry do not matter; two calls that overlap in time must not
+ * share a workspace.
  */
 int paged_attention_decode_splitkv(void* out, int out_dtype, const void* query,
                                    const void* key_cache, const void* value_cache, int kv_dtype,
@@ -145,8 +146,9 @@ int paged_attention_decode_splitkv(void* out, int out_dtype, const void* query,
                                    void* stream);
 
 /*
- * The two halves of paged_attention_decode_splitkv, for callers that schedule
- * or combine them themselves (e.g. to merge partials of several passes).
+ * The two halves of paged_attention_decode_splitkv as separate launches, for
+ * callers that schedule or combine them themselves (e.g. to merge partials of
+ * several passes).
  *
  * paged_attention_decode_splitkv_partials launches only the partition kernel.
  * Workspace layout (float32, rows = batch * q_len * num_q_heads in
@@ -156,11 +158,11 @@ int paged_attention_decode_splitkv(void* out, int out_dtype, const void* query,
  *                         (-inf if the row sees no position in the partition)
  *   l[rows][P]            sum_j 2^(s_j - m)
  * Partition p covers positions [p * partition_size, (p+1) * partition_size),
- * the last one runs to the end of the sequence; partitions that start at or
- * past a sequence's length are not written.
+ * the last one runs to the end of the sequence; a partition that starts at or
+ * past a sequence's (clamped) length gets m = -inf, l = 0 and no o.
  *
- * paged_attention_decode_splitkv_merge reads those partials (only partitions
- * that start before each sequence's clamped length) and writes
+ * paged_attention_decode_splitkv_merge reads the P partials of every row
+ * (skipping those with m = -inf) and writes
  * out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p with M = max_p m_p
  * (zeros where no partition saw a position).
  */
@@ -173,8 +175,7 @@ int paged_attention_decode_splitkv_partials(const void* query, const void* key_c
                                             int max_context_len, int partition_size,
                                             void* workspace, size_t workspace_bytes, void* stream);
 
-int paged_attention_decode_splitkv_merge(void* out, int out_dtype, const int32_t* context_lens,
-                                         int max_blocks_per_seq, int batch, int q_len,
+int paged_attention_decode_splitkv_merge(void* out, int out_dtype, int batch, int q_len,
                                          int num_q_heads, int head_dim, int max_context_len,
                                          int partition_size, const void* workspace,
                                          size_t workspace_bytes, void* stream);

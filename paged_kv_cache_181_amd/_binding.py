@@ -60,8 +60,7 @@ SIGNATURES = {
     "kv_cache_bytes_per_token": ([_i, _i, _i, _i, ctypes.POINTER(_i64)], _i),
     "paged_attention_decode_splitkv_partials": (_ATTN[2:] + [_i, _i, _p, _sz, _p], _i),
     "paged_attention_decode_splitkv_k8v4_partials": (_ATTN_K8V4[2:] + [_i, _i, _p, _sz, _p], _i),
-    "paged_attention_decode_splitkv_merge": ([_p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p, _sz, _p],
-                                             _i),
+    "paged_attention_decode_splitkv_merge": ([_p, _i, _i, _i, _i, _i, _i, _i, _p, _sz, _p], _i),
 }
 for _name, (_args, _res) in SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -289,15 +288,12 @@ def paged_attention_decode_splitkv_k8v4_partials(query, k_cache, k_scale, v_cach
         int(partition_size), _ptr(workspace), nbytes, _stream(dev)))
 
 
-def paged_attention_decode_splitkv_merge(out, context_lens, max_blocks_per_seq, max_context_len,
-                                         partition_size, workspace):
+def paged_attention_decode_splitkv_merge(out, max_context_len, partition_size, workspace):
     """Log-sum-exp merge of the partials in ``workspace`` into ``out`` [B, Q, Hq, D]."""
-    torch = _torch()
-    dev = _dev(out, context_lens, workspace)
+    dev = _dev(out, workspace)
     _expect(out.dim() == 4, "out must be [B, Q, Hq, D]")
     B, Q, Hq, D = out.shape
-    _expect(context_lens.dtype == torch.int32 and context_lens.shape == (B,), "context_lens int32 [B]")
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib.paged_attention_decode_splitkv_merge(
-        _ptr(out), _dtype_code(out), _ptr(context_lens), int(max_blocks_per_seq), B, Q, Hq, D,
-        int(max_context_len), int(partition_size), _ptr(workspace), nbytes, _stream(dev)))
+        _ptr(out), _dtype_code(out), B, Q, Hq, D, int(max_context_len), int(partition_size),
+        _ptr(workspace), nbytes, _stream(dev)))

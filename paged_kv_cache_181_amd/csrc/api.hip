@@ -367,12 +367,11 @@ int paged_attention_decode_splitkv_k8v4_partials(
                        "paged_attention_decode_splitkv_k8v4_partials");
 }
 
-int paged_attention_decode_splitkv_merge(void* out, int out_dtype, const int32_t* context_lens,
-                                         int max_blocks_per_seq, int batch, int q_len,
+int paged_attention_decode_splitkv_merge(void* out, int out_dtype, int batch, int q_len,
                                          int num_q_heads, int head_dim, int max_context_len,
                                          int partition_size, const void* workspace,
                                          size_t workspace_bytes, void* stream) {
-  if (batch < 0 || q_len <= 0 || num_q_heads <= 0 || max_blocks_per_seq < 0)
+  if (batch < 0 || q_len <= 0 || num_q_heads <= 0)
     return fail(PKV_ERR_SHAPE, "batch >= 0, q_len > 0, num_q_heads > 0 required");
   if (head_dim != 64 && head_dim != 128)
     return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
@@ -385,7 +384,7 @@ int paged_attention_decode_splitkv_merge(void* out, int out_dtype, const int32_t
                           parts, need);
   if (rc) return rc;
   if (batch == 0) return ok();
-  if (!out || !context_lens) return fail(PKV_ERR_NULL, "a required pointer is NULL");
+  if (!out) return fail(PKV_ERR_NULL, "out is NULL");
   if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace is NULL");
   if (!aligned16(workspace)) return fail(PKV_ERR_ALIGN, "workspace must be 16-byte aligned");
   if (workspace_bytes < need)
@@ -394,8 +393,6 @@ int paged_attention_decode_splitkv_merge(void* out, int out_dtype, const int32_t
   pkv::AttnArgs a{};
   a.out = out;
   a.out_dtype = out_dtype;
-  a.context_lens = context_lens;
-  a.max_blocks = max_blocks_per_seq;
   a.batch = batch;
   a.q_len = q_len;
   a.num_q_heads = num_q_heads;

@@ -44,7 +44,6 @@
 
 namespace pkv {
 
-constexpr int NW = 4;                  // wavefronts per workgroup
 constexpr float kNegInf = -INFINITY;
 
 // Head dims of the K/Q operand held by quarter qd at QK step m (8 consecutive).
@@ -117,25 +116,69 @@ __device__ __forceinline__ void load_block(const AttnArgs& a, int64_t pb, int g,
   }
 }
 
-template <Fmt KV, Fmt QT, int D>
-struct AttnSmem {
-  static constexpr int VSTR = D + 4;                       // halves per staged V row
-  static constexpr int GR = D / 32;                        // V groups per row
-  static constexpr int VST = NW * 16 * VSTR * 2;           // staged V bytes
-  static constexpr int SIDE = KV == Fmt::K8V4 ? NW * 16 * (1 + 2 * GR) * 4 : 0;
-  static constexpr int MO = NW * 16 * D * 4;               // merge: per-wave outputs
-  static constexpr int BYTES = (VST + SIDE) > MO ? (VST + SIDE) : MO;
+// Workgroup shape: RT query rows per KV head tile (4 when G*q_len <= 4, else
+// 16).  The 16-bit 4-row form runs 8 wavefronts at 4 per SIMD (128 registers);
+// the K8/V4 and 16-row forms, which hold more per lane, 4 wavefronts at 3.
+template <Fmt KV, int RT> struct Shape {
+  static constexpr bool WIDE = RT == 4 && KV != Fmt::K8V4;
+  static constexpr int NW = WIDE ? 8 : 4;
+  static constexpr int WAVES_PER_SIMD = WIDE ? 4 : 3;
 };
 
-template <Fmt KV, Fmt QT, int D>
-__global__ __launch_bounds__(NW * kWave) void attn_partition_kernel(const AttnArgs a) {
+template <Fmt KV, int D, int RT>
+struct AttnSmem {
+  static constexpr int NW = Shape<KV, RT>::NW;
+  static constexpr int GR = D / 32;                        // V groups per row
+  static constexpr int VT = 16 * D * 2;                    // one staged V tile (bytes)
+  static constexpr int VST = NW * VT;
+  static constexpr int SIDE = KV == Fmt::K8V4 ? NW * 16 * (1 + 2 * GR) * 4 : 0;
+  static constexpr int MO = NW * RT * D * 4;               // merge: per-wave outputs
+  static constexpr int LOOP = VST + SIDE;
+  static constexpr int BYTES = LOOP > MO ? LOOP : MO;
+  static constexpr int QSTR = D + 8;                       // halves per staged query row
+};
+
+// Max over lanes l, l^16, l^32, l^48 (the four quarters) without the LDS path.
+__device__ __forceinline__ float quarter_max(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float quarter_sum(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Transposing LDS read (gfx950): within each group of 16 lanes, lane j gets
+// element j%4 of the 8-byte chunks addressed by lanes 4e + j/4, e = 0..3.
+__device__ __forceinline__ u2 lds_read_tr16(const unsigned char* p) {
+  typedef short s4v __attribute__((ext_vector_type(4)));
+  s4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s4v*)(p));
+  return __builtin_bit_cast(u2, v);
+}
+
+// The running max of a row only moves when a block's max exceeds it by more
+// than this (log2 units), so rescaling the accumulators is rare; weights are
+// then at most 2^8, well inside fp16/bf16 range.
+constexpr float kRescaleSlack = 8.f;
+
+template <Fmt KV, Fmt QT, int D, int RT>
+__global__ __launch_bounds__((Shape<KV, RT>::NW * kWave), (Shape<KV, RT>::WAVES_PER_SIMD))
+void attn_partition_kernel(const AttnArgs a) {
   using MM = Mma<QT>;
-  using SM = AttnSmem<KV, QT, D>;
+  using SM = AttnSmem<KV, D, RT>;
+  constexpr int NW = SM::NW;
   constexpr int KS = D / 32;           // QK MFMA steps
   constexpr int NT = D / 16;           // PV output tiles
-  constexpr int VSTR = SM::VSTR;
   constexpr int GR = SM::GR;
+  constexpr int QSTR = SM::QSTR;
   __shared__ __align__(16) unsigned char smem[SM::BYTES];
+  __shared__ __align__(16) uint16_t q_s[16 * QSTR];
   __shared__ float mm_s[NW][16], ml_s[NW][16];
 
   const int lane = threadIdx.x & 63;
@@ -149,26 +192,68 @@ __global__ __launch_bounds__(NW * kWave) void attn_partition_kernel(const AttnAr
   L = min(max(L, 0), a.max_blocks * kBlock);
   const int nblk = (L + kBlock - 1) / kBlock;
   const int bb = p * a.part_blocks;
-  if (split && bb >= nblk) return;                          // partition past this sequence
+  if (split && bb >= nblk) {                                // partition past this sequence:
+    // mark it empty (max -inf, sum 0) so the merge can read every partition
+    // without first reading the sequence length
+    for (int rr = threadIdx.x; rr < GQ; rr += NW * kWave) {
+      const int64_t pi = (((int64_t)b * Q + rr / G) * Hq + g * G + rr % G) * a.num_parts + p;
+      a.ws_m[pi] = kNegInf;
+      a.ws_l[pi] = 0.f;
+    }
+    return;
+  }
   const int be = (p == a.num_parts - 1) ? nblk : min(nblk, bb + a.part_blocks);
+
+  // This wave's blocks are bb + w + NW*k, k = 0 .. nmine-1.  Their table
+  // entries are read 64 at a time into one VGPR (lane j holds entry j of the
+  // chunk) and picked out with readlane, so no table load sits between the
+  // K/V loads of consecutive blocks.  The first chunk is requested before
+  // anything else: issued later it would queue behind the K/V stream of the
+  // waves that started first.
+  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
+  const int nmine = be > bb + w ? (be - bb - w + NW - 1) / NW : 0;
+  int tbl_next = lane < nmine ? bt[bb + w + NW * lane] : 0;
 
   // the query row this lane owns: rho = iq * G + hl
   const bool row_ok = rho < GQ;
   const int iq = row_ok ? rho / G : 0;
-  const int h = g * G + (row_ok ? rho % G : 0);
   const int nvis = row_ok ? (L - Q + iq + 1) : L;           // visible positions of the row
   const int full_lim = L - Q + 1;                           // every row sees j < full_lim
 
-  u4 qop[KS];
-  {
-    const uint16_t* qp = (const uint16_t*)a.q + (((int64_t)b * Q + iq) * Hq + h) * D;
-#pragma unroll
-    for (int m = 0; m < KS; ++m)
-      qop[m] = row_ok ? *(const u4*)(qp + qk_dim<KV>(m, qd)) : u4{0u, 0u, 0u, 0u};
+  // ---- the first block's K/V loads go out before the query is staged
+  int tblv = tbl_next;
+  if (64 < nmine) {
+    const int kk = 64 + lane;
+    tbl_next = kk < nmine ? bt[bb + w + NW * kk] : 0;
   }
+  auto fetch = [&](int j, BlockRegs<KV, D>& br) -> bool {
+    const int pb = __builtin_amdgcn_readlane(tblv, j);
+    const bool ok = pb >= 0 && (int64_t)pb < a.num_blocks;
+    load_block<KV, D>(a, ok ? pb : 0, g, rho, qd, br);
+    return ok;
+  };
+  BlockRegs<KV, D> r0, r1;
+  bool ok0 = false, ok1 = false;
+  if (nmine > 0) ok0 = fetch(0, r0);
 
-  uint16_t* vst = (uint16_t*)smem + w * 16 * VSTR;          // this wave's staged V tile
+  // ---- the 16 query rows of this KV head, staged once in LDS (zero rows
+  // past G*q_len); each wave reads its MFMA operand from there per block
+  for (int idx = threadIdx.x; idx < 16 * (D / 8); idx += NW * kWave) {
+    const int r = idx / (D / 8), c8 = idx % (D / 8);
+    u4 v = u4{0u, 0u, 0u, 0u};
+    if (r < GQ) {
+      const int h = g * G + r % G;
+      v = *(const u4*)((const uint16_t*)a.q + (((int64_t)b * Q + r / G) * Hq + h) * D + 8 * c8);
+    }
+    *(u4*)(q_s + r * QSTR + 8 * c8) = v;
+  }
+  __syncthreads();
+
+  unsigned char* vst = smem + w * (16 * D * 2);             // this wave's staged V tile
   float* side = (float*)(smem + SM::VST) + w * 16 * (1 + 2 * GR);   // K8/V4 scales
+  // byte offset of this lane's 8-byte chunk for the transposing V read:
+  // token 4*qd + (rho>>2), dims 4*(rho&3) .. +3 of the 16-dim tile
+  const int tr_off = ((((rho & 3) >> 1) * 16) + 4 * qd + (rho >> 2)) * 16 + (rho & 1) * 8;
 
   float m_run = kNegInf, l_run = 0.f;
   f4 o[NT];
@@ -178,21 +263,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_partition_kernel(const AttnAr
 #pragma unroll
   for (int gi = 0; gi < GR; ++gi) zacc[gi] = 0.f;
 
-  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
   const float sl2 = a.scale_log2;
-
-  // This wave's blocks are bb + w + NW*k, k = 0 .. nmine-1.  Their table
-  // entries are read 64 at a time into one VGPR (lane j holds entry j of the
-  // chunk) and picked out with readlane, so no table load sits between the
-  // K/V loads of consecutive blocks.
-  const int nmine = be > bb + w ? (be - bb - w + NW - 1) / NW : 0;
-  int tblv = 0;
-  auto fetch = [&](int j, BlockRegs<KV, D>& br) -> bool {
-    const int pb = __builtin_amdgcn_readlane(tblv, j);
-    const bool ok = pb >= 0 && (int64_t)pb < a.num_blocks;
-    load_block<KV, D>(a, ok ? pb : 0, g, rho, qd, br);
-    return ok;
-  };
 
   auto process = [&](int i, bool ok, BlockRegs<KV, D>& br) {
     const int j0 = i * kBlock;
@@ -200,13 +271,41 @@ __global__ __launch_bounds__(NW * kWave) void attn_partition_kernel(const AttnAr
     const bool full = ok && j0 + kBlock <= full_lim;         // no masking needed at all
     const bool tok_ok = ok && j0 + rho < L;                  // this lane's token (rho) exists
 
+    // ---- stage V in load-lane order: the 16-byte chunk (m, c) of token t at
+    // m*1024 + (16c + t)*16, i.e. lane (t, c) of load m writes where it read.
+    // Rows past the length are zeroed (their weight is 0, and 0 * NaN is NaN).
+    if constexpr (KV == Fmt::K8V4) {
+      constexpr int NC = D / 4;                 // codes held by this lane: dims NC*qd ..
+      const uint32_t wd[4] = {br.v.x, br.v.y, br.v.z, br.v.w};
+#pragma unroll
+      for (int q = 0; q < NC / 8; ++q) {        // 8 codes -> one 16-byte chunk
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t byte = (wd[q] >> (8 * e)) & 0xffu;
+          const int c0 = tok_ok ? (int)(byte & 0xfu) : 0;
+          const int c1 = tok_ok ? (int)(byte >> 4) : 0;
+          pk[e] = pack2_codes<QT>(c0, c1);
+        }
+        const int dim0 = NC * qd + 8 * q;      // first dim of this chunk
+        *(u4*)(vst + (dim0 >> 5) * 1024 + (16 * ((dim0 & 31) >> 3) + rho) * 16) =
+            u4{pk[0], pk[1], pk[2], pk[3]};
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < KS; ++m) {
+        u4 vv = br.v[m];
+        if (tail && !tok_ok) vv = u4{0u, 0u, 0u, 0u};
+        *(u4*)(vst + m * 1024 + lane * 16) = vv;
+      }
+    }
+
     // ---- scores S^T = K Q^T
     f4 s = f4{0.f, 0.f, 0.f, 0.f};
     if constexpr (KV == Fmt::K8V4) {
 #pragma unroll
       for (int u = 0; u < D / 64; ++u) {
         const u4 c = br.k[u];
-        u4 lo, hi;
         const uint32_t wd[4] = {c.x, c.y, c.z, c.w};
         uint32_t cv[8];
 #pragma unroll
@@ -215,12 +314,12 @@ __global__ __launch_bounds__(NW * kWave) void attn_partition_kernel(const AttnAr
           cv[2 * q] = pack2_codes<QT>((int8_t)(x & 0xff), (int8_t)((x >> 8) & 0xff));
           cv[2 * q + 1] = pack2_codes<QT>((int8_t)((x >> 16) & 0xff), (int8_t)((x >> 24) & 0xff));
         }
-        lo = u4{cv[0], cv[1], cv[2], cv[3]};
-        hi = u4{cv[4], cv[5], cv[6], cv[7]};
-        s = MM::qk(lo, qop[2 * u], s);
-        s = MM::qk(hi, qop[2 * u + 1], s);
+        const u4 q0 = *(const u4*)(q_s + rho * QSTR + qk_dim<KV>(2 * u, qd));
+        const u4 q1 = *(const u4*)(q_s + rho * QSTR + qk_dim<KV>(2 * u + 1, qd));
+        s = MM::qk(u4{cv[0], cv[1], cv[2], cv[3]}, q0, s);
+        s = MM::qk(u4{cv[4], cv[5], cv[6], cv[7]}, q1, s);
       }
-      // per-token K scales and V scale/zero, redistributed through LDS from the
+      // per-token K scales and V scale/zero, moved through LDS from the
       // token-owner layout (lane rho) to the score layout (tokens 4*qd + r)
       if (qd == 0) {
         side[rho] = f16_bits_to_f32(br.ks);
@@ -236,40 +335,14 @@ __global__ __launch_bounds__(NW * kWave) void attn_partition_kernel(const AttnAr
       }
     } else {
 #pragma unroll
-      for (int m = 0; m < KS; ++m) s = MM::qk(br.k[m], qop[m], s);
-    }
-
-    // ---- stage V (natural [token][dim] layout), zeroing rows past the length
-    if constexpr (KV == Fmt::K8V4) {
-      constexpr int NC = D / 4;                 // codes held by this lane: dims NC*qd ..
-      const uint32_t wd[4] = {br.v.x, br.v.y, br.v.z, br.v.w};
-#pragma unroll
-      for (int q = 0; q < NC / 8; ++q) {
-        uint32_t pk[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t byte = (wd[q] >> (8 * e)) & 0xffu;
-          const int c0 = tok_ok ? (int)(byte & 0xfu) : 0;
-          const int c1 = tok_ok ? (int)(byte >> 4) : 0;
-          pk[e] = pack2_codes<QT>(c0, c1);
-        }
-        uint16_t* dst = vst + rho * VSTR + NC * qd + 8 * q;
-        *(u2*)(dst) = u2{pk[0], pk[1]};
-        *(u2*)(dst + 4) = u2{pk[2], pk[3]};
-      }
-    } else {
-#pragma unroll
       for (int m = 0; m < KS; ++m) {
-        u4 vv = br.v[m];
-        if (tail && !tok_ok) vv = u4{0u, 0u, 0u, 0u};
-        uint16_t* dst = vst + rho * VSTR + 32 * m + 8 * qd;
-        *(u2*)(dst) = u2{vv.x, vv.y};
-        *(u2*)(dst + 4) = u2{vv.z, vv.w};
+        const u4 qm = *(const u4*)(q_s + rho * QSTR + qk_dim<KV>(m, qd));
+        s = MM::qk(br.k[m], qm, s);
       }
     }
     wave_lds_fence();
 
-    // ---- online softmax in the exp2 domain
+    // ---- online softmax in the exp2 domain (lane: row rho, tokens 4*qd + r)
     float sv[4];
     if constexpr (KV == Fmt::K8V4) {
 #pragma unroll
@@ -285,21 +358,27 @@ __global__ __launch_bounds__(NW * kWave) void attn_partition_kernel(const AttnAr
         if (!ok || j >= nvis) sv[r] = kNegInf;
       }
     }
-    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mx = fmaxf(mx, wave_xor(mx, 16));
-    mx = fmaxf(mx, wave_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    const float mx = quarter_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+    const bool grow = mx > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(grow)) {                 // rare: move the reference max
+      // rows that do not grow keep their max (alpha 1: never -inf - -inf);
+      // a growing row from -inf gets alpha 0
+      const float m_new = grow ? mx : m_run;
+      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
+#pragma unroll
+      for (int n = 0; n < NT; ++n) o[n] *= alpha;
+      l_run *= alpha;
+#pragma unroll
+      for (int gi = 0; gi < GR; ++gi) zacc[gi] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
     float pr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sv[r] - m_use);
-    l_run = l_run * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    m_run = m_new;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) o[n] *= alpha;
+    l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T; the V operand comes from one transposing read per tile
     if constexpr (KV == Fmt::K8V4) {
 #pragma unroll
       for (int gi = 0; gi < GR; ++gi) {
@@ -311,15 +390,13 @@ __global__ __launch_bounds__(NW * kWave) void attn_partition_kernel(const AttnAr
           pw[r] = pr[r] * sd[0];
           zs += pr[r] * sd[1];
         }
-        zacc[gi] = zacc[gi] * alpha + zs;
+        zacc[gi] += zs;
         u2 phi, plo;
         MM::split(pw, phi, plo);
 #pragma unroll
         for (int nn = 0; nn < 2; ++nn) {
           const int n = 2 * gi + nn;
-          const uint16_t* src = vst + (4 * qd) * VSTR + 16 * n + rho;
-          const u2 av = u2{(uint32_t)src[0] | ((uint32_t)src[VSTR] << 16),
-                           (uint32_t)src[2 * VSTR] | ((uint32_t)src[3 * VSTR] << 16)};
+          const u2 av = lds_read_tr16(vst + tr_off + (n >> 1) * 1024 + (n & 1) * 512);
           o[n] = MM::pv(av, phi, o[n]);
           o[n] = MM::pv(av, plo, o[n]);
         }
@@ -329,9 +406,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_partition_kernel(const AttnAr
       MM::split(pr, phi, plo);
 #pragma unroll
       for (int n = 0; n < NT; ++n) {
-        const uint16_t* src = vst + (4 * qd) * VSTR + 16 * n + rho;
-        const u2 av = u2{(uint32_t)src[0] | ((uint32_t)src[VSTR] << 16),
-                         (uint32_t)src[2 * VSTR] | ((uint32_t)src[3 * VSTR] << 16)};
+        const u2 av = lds_read_tr16(vst + tr_off + (n >> 1) * 1024 + (n & 1) * 512);
         o[n] = MM::pv(av, phi, o[n]);
         o[n] = MM::pv(av, plo, o[n]);
       }
@@ -345,10 +420,15 @@ __global__ __launch_bounds__(NW * kWave) void attn_partition_kernel(const AttnAr
   // before each block covers only that block's loads.
   for (int c0 = 0; c0 < nmine; c0 += 64) {
     const int cnt = min(64, nmine - c0);
-    tblv = lane < cnt ? bt[bb + w + NW * (c0 + lane)] : 0;
+    if (c0 > 0) {
+      tblv = tbl_next;
+      if (c0 + 64 < nmine) {                          // next chunk, one chunk ahead
+        const int kk = c0 + 64 + lane;
+        tbl_next = kk < nmine ? bt[bb + w + NW * kk] : 0;
+      }
+      ok0 = fetch(0, r0);
+    }
     const int i0 = bb + w + NW * c0;
-    BlockRegs<KV, D> r0, r1;
-    bool ok0 = fetch(0, r0), ok1 = false;
     int k = 0;
     for (int pr = (cnt - 1) >> 1; pr > 0; --pr) {     // branch-free pairs of blocks
       ok1 = fetch(k + 1, r1);
@@ -367,14 +447,10 @@ __global__ __launch_bounds__(NW * kWave) void attn_partition_kernel(const AttnAr
   }
 
   // ---- per-wave totals: the sum is spread over the four quarters
-  l_run += wave_xor(l_run, 16);
-  l_run += wave_xor(l_run, 32);
+  l_run = quarter_sum(l_run);
   if constexpr (KV == Fmt::K8V4) {
 #pragma unroll
-    for (int gi = 0; gi < GR; ++gi) {
-      zacc[gi] += wave_xor(zacc[gi], 16);
-      zacc[gi] += wave_xor(zacc[gi], 32);
-    }
+    for (int gi = 0; gi < GR; ++gi) zacc[gi] = quarter_sum(zacc[gi]);
 #pragma unroll
     for (int n = 0; n < NT; ++n) o[n] += zacc[n / 2];
   }
@@ -382,11 +458,11 @@ __global__ __launch_bounds__(NW * kWave) void attn_partition_kernel(const AttnAr
   // ---- merge the NW wavefronts of this workgroup (LDS reused)
   __syncthreads();
   float* mo = (float*)smem;
-  if (row_ok) {
+  if (rho < RT && row_ok) {
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mo[(w * 16 + rho) * D + 16 * n + 4 * qd + r] = o[n][r];
+      for (int r = 0; r < 4; ++r) mo[(w * RT + rho) * D + 16 * n + 4 * qd + r] = o[n][r];
   }
   if (qd == 0) {
     mm_s[w][rho] = m_run;
@@ -403,7 +479,7 @@ __global__ __launch_bounds__(NW * kWave) void attn_partition_kernel(const AttnAr
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) {
       const float e = fast_exp2(mm_s[ww][rr] - Mu);
-      num += e * mo[(ww * 16 + rr) * D + d];
+      num += e * mo[(ww * RT + rr) * D + d];
       den += e * ml_s[ww][rr];
     }
     const int64_t orow = ((int64_t)b * Q + rr / G) * Hq + g * G + rr % G;
@@ -422,54 +498,68 @@ __global__ __launch_bounds__(NW * kWave) void attn_partition_kernel(const AttnAr
 
 // Log-sum-exp merge of the split-KV partials: one workgroup per output row
 // (b, i, h).  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, M = max_p m_p.
+// Single pass: thread (c, grp) takes partitions grp, grp+NG, ... for the 4
+// dims of chunk c, folding each into a running (max, sum, acc) so every load
+// can be in flight at once; the NG running states are then combined in LDS.
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
   constexpr int NC = D / 4;              // float4 chunks per row
   constexpr int NG = 256 / NC;           // partition groups
-  __shared__ float red[256];
   __shared__ f4 acc_s[NG][NC];
-  __shared__ float den_s[NG];
+  __shared__ float m_s[NG], den_s[NG];
 
   const int64_t row = blockIdx.x;
   const int t = threadIdx.x;
-  const int b = (int)(row / ((int64_t)a.q_len * a.num_q_heads));
-  int L = a.context_lens[b];
-  L = min(max(L, 0), a.max_blocks * kBlock);
-  const int nblk = (L + kBlock - 1) / kBlock;
-  const int np = nblk == 0 ? 0 : min((nblk + a.part_blocks - 1) / a.part_blocks, a.num_parts);
+  // every partition of the grid holds a partial or an empty marker (max -inf)
+  const int np = a.num_parts;
   const float* wm = a.ws_m + row * a.num_parts;
   const float* wl = a.ws_l + row * a.num_parts;
   const float* wo = a.ws_o + row * a.num_parts * D;
 
-  float M = kNegInf;
-  for (int pp = t; pp < np; pp += 256) M = fmaxf(M, wm[pp]);
-  red[t] = M;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if (t < s) red[t] = fmaxf(red[t], red[t + s]);
-    __syncthreads();
-  }
-  M = red[0];
-  const float Mu = M == kNegInf ? 0.f : M;
-
   const int c = t % NC, grp = t / NC;
+  float m_t = kNegInf, den = 0.f;
   f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-  for (int pp = grp; pp < np; pp += NG) {
-    const float e = fast_exp2(wm[pp] - Mu);
-    acc += e * *(const f4*)(wo + (int64_t)pp * D + 4 * c);
-    den += e * wl[pp];
+  constexpr int U = 8;                   // partitions whose loads are issued together
+  for (int p0 = grp; p0 < np; p0 += U * NG) {
+    float mp[U], lp[U];
+    f4 op[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {        // loads first (clamped index), no branches between
+      const int pp = min(p0 + u * NG, np - 1);
+      mp[u] = wm[pp];
+      lp[u] = wl[pp];
+      op[u] = *(const f4*)(wo + (int64_t)pp * D + 4 * c);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool use = p0 + u * NG < np && mp[u] != kNegInf;   // -inf: partition saw nothing
+      const float m_new = use ? fmaxf(m_t, mp[u]) : m_t;
+      const float e_old = (!use || m_t == kNegInf) ? (use ? 0.f : 1.f) : fast_exp2(m_t - m_new);
+      const float e_new = use ? fast_exp2(mp[u] - m_new) : 0.f;
+      acc = acc * e_old + op[u] * e_new;
+      den = den * e_old + lp[u] * e_new;
+      m_t = m_new;
+    }
   }
   acc_s[grp][c] = acc;
-  if (c == 0) den_s[grp] = den;
+  if (c == 0) {
+    m_s[grp] = m_t;
+    den_s[grp] = den;
+  }
   __syncthreads();
   if (t < NC) {
+    float M = kNegInf;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) M = fmaxf(M, m_s[gg]);
     f4 tot = f4{0.f, 0.f, 0.f, 0.f};
     float dt = 0.f;
+    if (M != kNegInf) {
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) {
-      tot += acc_s[gg][t];
-      dt += den_s[gg];
+      for (int gg = 0; gg < NG; ++gg) {
+        const float e = m_s[gg] == kNegInf ? 0.f : fast_exp2(m_s[gg] - M);
+        tot += acc_s[gg][t] * e;
+        dt += den_s[gg] * e;
+      }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -488,7 +578,13 @@ template <Fmt KV, Fmt QT, int D>
 static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream, int stage) {
   if (stage != STAGE_MERGE) {
     const dim3 grid((unsigned)a.num_parts, (unsigned)a.num_kv_heads, (unsigned)a.batch);
-    hipLaunchKernelGGL((attn_partition_kernel<KV, QT, D>), grid, dim3(NW * kWave), 0, stream, a);
+    if (a.gqa * a.q_len <= 4) {
+      hipLaunchKernelGGL((attn_partition_kernel<KV, QT, D, 4>), grid,
+                         dim3(Shape<KV, 4>::NW * kWave), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((attn_partition_kernel<KV, QT, D, 16>), grid,
+                         dim3(Shape<KV, 16>::NW * kWave), 0, stream, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.ws_o == nullptr || stage == STAGE_PARTIALS) return e;
   }

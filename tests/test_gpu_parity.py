@@ -314,7 +314,7 @@ def test_k8v4_decode_matches_oracle_on_the_same_codes(P, full, split):
         if split:
             mcl = int(case.context_lens.max())
             n = P.splitkv_workspace_size(*q.shape[:3], q.shape[3], mcl, 512)
-            ws = torch.empty(n // 4 + 4, dtype=torch.float32, device="cuda")
+            ws = torch.zeros(n // 4 + 4, dtype=torch.float32, device="cuda")
             P.paged_attention_decode_splitkv_k8v4(out, q, *args, mcl, 512, ws)
         else:
             P.paged_attention_decode_k8v4(out, q, *args)
@@ -351,3 +351,28 @@ def test_errors_launch_nothing(P):
                                          512, torch.empty(4, device="cuda"))
     assert e.value.code == -4
     assert not out.any().item()
+
+
+def test_workspace_reuse_and_two_launch_path(P):
+    """Back-to-back split-KV calls on one workspace with fresh queries each
+    time must match the separately launched halves (partials, then merge)."""
+    case, _ = get_case("llama8b_batch")
+    dc = DevCase(case)
+    B, Q, Hq, D = dc.q.shape
+    mcl = int(case.context_lens.max())
+    n = P.splitkv_workspace_size(B, Q, Hq, D, mcl, 512)
+    ws = torch.zeros(n // 4, dtype=torch.float32, device="cuda")
+    ws2 = torch.zeros_like(ws)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    for it in range(20):
+        q = torch.randn(dc.q.shape, generator=gen, device="cuda", dtype=dc.q.dtype)
+        fused = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+        P.paged_attention_decode_splitkv(fused, q, dc.k, dc.v, dc.bt, dc.cl, case.scale, 4, mcl, 512,
+                                         ws)
+        two = torch.empty_like(fused)
+        P.paged_attention_decode_splitkv_partials(q, dc.k, dc.v, dc.bt, dc.cl, case.scale, 4, mcl, 512,
+                                                  ws2)
+        P.paged_attention_decode_splitkv_merge(two, mcl, 512, ws2)
+        torch.cuda.synchronize()
+        assert torch.equal(fused, two), it
