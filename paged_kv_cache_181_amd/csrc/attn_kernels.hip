@@ -9,7 +9,7 @@
 //
 // Work decomposition
 //   grid = (partition, KV head, sequence); a workgroup of NW wavefronts owns the
-//   blocks of one partition; wavefront w takes blocks w, w+NW, ... of it.  All
+//   blocks of one partition; wavefront w takes a contiguous run of them.  All
 //   G*q_len query rows that share a KV head live in one wavefront, so each K/V
 //   byte is read from HBM once.  The direct form is the same kernel with one
 //   partition per sequence; the split-KV form writes per-partition partials and
@@ -178,7 +178,7 @@ void attn_partition_kernel(const AttnArgs a) {
   constexpr int GR = SM::GR;
   constexpr int QSTR = SM::QSTR;
   __shared__ __align__(16) unsigned char smem[SM::BYTES];
-  __shared__ __align__(16) uint16_t q_s[16 * QSTR];
+  __shared__ __align__(16) uint16_t q_s[NW * RT * QSTR];
   __shared__ float mm_s[NW][16], ml_s[NW][16];
 
   const int lane = threadIdx.x & 63;
@@ -188,10 +188,38 @@ void attn_partition_kernel(const AttnArgs a) {
   const int Q = a.q_len, G = a.gqa, GQ = G * Q, Hq = a.num_q_heads;
   const bool split = a.ws_o != nullptr;
 
+  // ---- loads that do not depend on the sequence length go out first and
+  // together: the table entries of this wave's first blocks, this wave's copy
+  // of the query rows, and the length.  Wave w owns the contiguous run of
+  // `per` blocks starting at bb + w*per (per depends on the partition size
+  // only, so a block's wave never depends on the length); lane j holds entry
+  // j of a 64-entry chunk of the run, picked out later with readlane, so no
+  // table load sits between the K/V loads of consecutive blocks.  Nothing
+  // waits on another wave before the first K/V loads.
+  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
+  const int bb = p * a.part_blocks;
+  int per = (a.part_blocks + NW - 1) / NW;
+  int tbl_next;
+  {
+    const int e = bb + w * per + lane;
+    tbl_next = lane < per && e < a.max_blocks ? bt[e] : 0;
+  }
+  constexpr int QCW = RT * (D / 8);                         // 16-byte query chunks per wave
+  constexpr int QPL = (QCW + kWave - 1) / kWave;            // per lane
+  u4 qv[QPL];
+#pragma unroll
+  for (int u = 0; u < QPL; ++u) {
+    const int idx = lane + u * kWave;
+    const int r = idx / (D / 8), c8 = idx % (D / 8);
+    qv[u] = u4{0u, 0u, 0u, 0u};
+    if (idx < QCW && r < GQ) {
+      const int h = g * G + r % G;
+      qv[u] = *(const u4*)((const uint16_t*)a.q + (((int64_t)b * Q + r / G) * Hq + h) * D + 8 * c8);
+    }
+  }
   int L = a.context_lens[b];
   L = min(max(L, 0), a.max_blocks * kBlock);
   const int nblk = (L + kBlock - 1) / kBlock;
-  const int bb = p * a.part_blocks;
   if (split && bb >= nblk) {                                // partition past this sequence:
     // mark it empty (max -inf, sum 0) so the merge can read every partition
     // without first reading the sequence length
@@ -203,28 +231,25 @@ void attn_partition_kernel(const AttnArgs a) {
     return;
   }
   const int be = (p == a.num_parts - 1) ? nblk : min(nblk, bb + a.part_blocks);
+  if (be - bb > a.part_blocks) {        // a last partition longer than the others
+    per = (be - bb + NW - 1) / NW;      // (length past the grid): runs resized
+    const int e = bb + w * per + lane;
+    tbl_next = lane < per && e < a.max_blocks ? bt[e] : 0;
+  }
+  const int w0 = bb + w * per;                              // first block of this wave's run
+  const int nmine = max(0, min(per, be - w0));
 
-  // This wave's blocks are bb + w + NW*k, k = 0 .. nmine-1.  Their table
-  // entries are read 64 at a time into one VGPR (lane j holds entry j of the
-  // chunk) and picked out with readlane, so no table load sits between the
-  // K/V loads of consecutive blocks.  The first chunk is requested before
-  // anything else: issued later it would queue behind the K/V stream of the
-  // waves that started first.
-  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
-  const int nmine = be > bb + w ? (be - bb - w + NW - 1) / NW : 0;
-  int tbl_next = lane < nmine ? bt[bb + w + NW * lane] : 0;
-
-  // the query row this lane owns: rho = iq * G + hl
+  // the query row this lane owns: rho = iq * G + hl (lanes past G*q_len
+  // compute a copy of a real row; their results are never written)
   const bool row_ok = rho < GQ;
   const int iq = row_ok ? rho / G : 0;
   const int nvis = row_ok ? (L - Q + iq + 1) : L;           // visible positions of the row
   const int full_lim = L - Q + 1;                           // every row sees j < full_lim
 
-  // ---- the first block's K/V loads go out before the query is staged
   int tblv = tbl_next;
   if (64 < nmine) {
     const int kk = 64 + lane;
-    tbl_next = kk < nmine ? bt[bb + w + NW * kk] : 0;
+    tbl_next = kk < nmine ? bt[w0 + kk] : 0;
   }
   auto fetch = [&](int j, BlockRegs<KV, D>& br) -> bool {
     const int pb = __builtin_amdgcn_readlane(tblv, j);
@@ -236,18 +261,15 @@ void attn_partition_kernel(const AttnArgs a) {
   bool ok0 = false, ok1 = false;
   if (nmine > 0) ok0 = fetch(0, r0);
 
-  // ---- the 16 query rows of this KV head, staged once in LDS (zero rows
-  // past G*q_len); each wave reads its MFMA operand from there per block
-  for (int idx = threadIdx.x; idx < 16 * (D / 8); idx += NW * kWave) {
-    const int r = idx / (D / 8), c8 = idx % (D / 8);
-    u4 v = u4{0u, 0u, 0u, 0u};
-    if (r < GQ) {
-      const int h = g * G + r % G;
-      v = *(const u4*)((const uint16_t*)a.q + (((int64_t)b * Q + r / G) * Hq + h) * D + 8 * c8);
-    }
-    *(u4*)(q_s + r * QSTR + 8 * c8) = v;
+  // ---- stage the query rows in this wave's own LDS area
+  uint16_t* qw = q_s + w * RT * QSTR;
+#pragma unroll
+  for (int u = 0; u < QPL; ++u) {
+    const int idx = lane + u * kWave;
+    if (idx < QCW) *(u4*)(qw + (idx / (D / 8)) * QSTR + 8 * (idx % (D / 8))) = qv[u];
   }
-  __syncthreads();
+  wave_lds_fence();
+  const uint16_t* qrow = qw + (row_ok ? rho : rho % GQ) * QSTR;   // this lane's operand row
 
   unsigned char* vst = smem + w * (16 * D * 2);             // this wave's staged V tile
   float* side = (float*)(smem + SM::VST) + w * 16 * (1 + 2 * GR);   // K8/V4 scales
@@ -314,8 +336,8 @@ void attn_partition_kernel(const AttnArgs a) {
           cv[2 * q] = pack2_codes<QT>((int8_t)(x & 0xff), (int8_t)((x >> 8) & 0xff));
           cv[2 * q + 1] = pack2_codes<QT>((int8_t)((x >> 16) & 0xff), (int8_t)((x >> 24) & 0xff));
         }
-        const u4 q0 = *(const u4*)(q_s + rho * QSTR + qk_dim<KV>(2 * u, qd));
-        const u4 q1 = *(const u4*)(q_s + rho * QSTR + qk_dim<KV>(2 * u + 1, qd));
+        const u4 q0 = *(const u4*)(qrow + qk_dim<KV>(2 * u, qd));
+        const u4 q1 = *(const u4*)(qrow + qk_dim<KV>(2 * u + 1, qd));
         s = MM::qk(u4{cv[0], cv[1], cv[2], cv[3]}, q0, s);
         s = MM::qk(u4{cv[4], cv[5], cv[6], cv[7]}, q1, s);
       }
@@ -336,7 +358,7 @@ void attn_partition_kernel(const AttnArgs a) {
     } else {
 #pragma unroll
       for (int m = 0; m < KS; ++m) {
-        const u4 qm = *(const u4*)(q_s + rho * QSTR + qk_dim<KV>(m, qd));
+        const u4 qm = *(const u4*)(qrow + qk_dim<KV>(m, qd));
         s = MM::qk(br.k[m], qm, s);
       }
     }
@@ -424,25 +446,25 @@ void attn_partition_kernel(const AttnArgs a) {
       tblv = tbl_next;
       if (c0 + 64 < nmine) {                          // next chunk, one chunk ahead
         const int kk = c0 + 64 + lane;
-        tbl_next = kk < nmine ? bt[bb + w + NW * kk] : 0;
+        tbl_next = kk < nmine ? bt[w0 + kk] : 0;
       }
       ok0 = fetch(0, r0);
     }
-    const int i0 = bb + w + NW * c0;
+    const int i0 = w0 + c0;
     int k = 0;
     for (int pr = (cnt - 1) >> 1; pr > 0; --pr) {     // branch-free pairs of blocks
       ok1 = fetch(k + 1, r1);
-      process(i0 + NW * k, ok0, r0);
+      process(i0 + k, ok0, r0);
       ok0 = fetch(k + 2, r0);
-      process(i0 + NW * (k + 1), ok1, r1);
+      process(i0 + k + 1, ok1, r1);
       k += 2;
     }
     if (k + 1 < cnt) {                                // two blocks left
       ok1 = fetch(k + 1, r1);
-      process(i0 + NW * k, ok0, r0);
-      process(i0 + NW * (k + 1), ok1, r1);
+      process(i0 + k, ok0, r0);
+      process(i0 + k + 1, ok1, r1);
     } else {                                          // one block left
-      process(i0 + NW * k, ok0, r0);
+      process(i0 + k, ok0, r0);
     }
   }
 
