@@ -68,6 +68,7 @@ int check_attention(void* out, int out_dtype, const void* query, const void* k_c
     return fail(PKV_ERR_UNSUPPORTED, "out_dtype must be PKV_F16, PKV_BF16 or PKV_F32");
   if (!std::isfinite(scale)) return fail(PKV_ERR_SHAPE, "scale must be finite");
   if (batch > 65535 || hkv > 65535) return fail(PKV_ERR_UNSUPPORTED, "batch or KV heads too large");
+  if (max_blocks > (1 << 26)) return fail(PKV_ERR_UNSUPPORTED, "max_blocks_per_seq above 2^26");
   if (batch == 0) return PKV_OK;
   if ((need_out && !out) || !query || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PKV_ERR_NULL, "a required pointer is NULL");

@@ -83,36 +83,94 @@ template <int D> struct BlockRegs<Fmt::K8V4, D> {
   u2 vs, vz;             // fp16 bits of the token's V scales / zeros (D/32 groups)
 };
 
-template <Fmt KV, int D>
-__device__ __forceinline__ void load_block(const AttnArgs& a, int64_t pb, int g, int rho, int qd,
-                                           BlockRegs<KV, D>& br) {
-  const int64_t row = (pb * kBlock + rho) * a.num_kv_heads + g;   // (block, token, head)
-  if constexpr (KV == Fmt::K8V4) {
-    const int8_t* kc = (const int8_t*)a.k_cache + row * D;
-#pragma unroll
-    for (int u = 0; u < D / 64; ++u) br.k[u] = *(const u4*)(kc + 64 * u + 16 * qd);
-    const uint8_t* vc = (const uint8_t*)a.v_cache + row * (D / 2);
-    if constexpr (D == 128) {
-      br.v = *(const u4*)(vc + 16 * qd);
-    } else {
-      u2 t = *(const u2*)(vc + 8 * qd);
-      br.v = u4{t.x, t.y, 0u, 0u};
-    }
-    br.ks = ((const uint16_t*)a.k_scale)[row];
-    if constexpr (D == 128) {
-      br.vs = *(const u2*)((const uint16_t*)a.v_scale + row * 4);
-      br.vz = *(const u2*)((const uint16_t*)a.v_zero + row * 4);
-    } else {
-      br.vs = u2{*(const uint32_t*)((const uint16_t*)a.v_scale + row * 2), 0u};
-      br.vz = u2{*(const uint32_t*)((const uint16_t*)a.v_zero + row * 2), 0u};
-    }
+// A buffer resource covering `bytes` bytes from `base` (wave-uniform): the
+// loads below are a scalar base plus a fixed 32-bit per-lane offset, and any
+// access past `bytes` reads 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Keeps a loop-invariant lane offset from being hoisted together with the
+// constant added to it, so the constant stays in the load's immediate field
+// instead of occupying a register of its own for the whole loop.
+__device__ __forceinline__ uint32_t pin(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  if constexpr (sizeof(T) == 16) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+  } else if constexpr (sizeof(T) == 8) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+  } else if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
   } else {
-    const uint16_t* kc = (const uint16_t*)a.k_cache + row * D;
-    const uint16_t* vc = (const uint16_t*)a.v_cache + row * D;
+    return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0));
+  }
+}
+
+// Byte offsets of this lane's data inside one block of one KV head (token rho,
+// quarter qd), and the byte size of one block of all KV heads.
+template <Fmt KV, int D>
+struct LaneOffsets {
+  uint32_t k, v, ks, vs;           // K codes/rows, V codes/rows, K scale, V scale/zero
+  uint32_t kblk, vblk, ksblk, vsblk;
+  __device__ __forceinline__ LaneOffsets(int hkv, int g, int rho, int qd) {
+    if constexpr (KV == Fmt::K8V4) {
+      k = (uint32_t)((rho * hkv + g) * D + 16 * qd);
+      v = (uint32_t)((rho * hkv + g) * (D / 2) + (D == 128 ? 16 : 8) * qd);
+      ks = (uint32_t)((rho * hkv + g) * 2);
+      vs = (uint32_t)((rho * hkv + g) * (D / 32) * 2);
+      kblk = (uint32_t)(kBlock * hkv * D);
+      vblk = (uint32_t)(kBlock * hkv * (D / 2));
+      ksblk = (uint32_t)(kBlock * hkv * 2);
+      vsblk = (uint32_t)(kBlock * hkv * (D / 32) * 2);
+    } else {
+      k = v = (uint32_t)(((rho * hkv + g) * D + 8 * qd) * 2);
+      ks = vs = 0;
+      kblk = vblk = (uint32_t)(kBlock * hkv * D * 2);
+      ksblk = vsblk = 0;
+    }
+  }
+};
+
+// Loads block pb (wave-uniform) into this lane's registers.  With `live`
+// false the loads are still issued (so the code has no branch around them)
+// but through zero-length resources: they return zeros and touch no memory.
+template <Fmt KV, int D>
+__device__ __forceinline__ void load_block(const AttnArgs& a, int64_t pb, bool live,
+                                           const LaneOffsets<KV, D>& lo, BlockRegs<KV, D>& br) {
+  const uint32_t on = live ? ~0u : 0u;
+  if constexpr (KV == Fmt::K8V4) {
+    const auto kr = span_rsrc((const char*)a.k_cache + pb * lo.kblk, lo.kblk & on);
+    const auto vr = span_rsrc((const char*)a.v_cache + pb * lo.vblk, lo.vblk & on);
+    const auto ksr = span_rsrc((const char*)a.k_scale + pb * lo.ksblk, lo.ksblk & on);
+    const auto vsr = span_rsrc((const char*)a.v_scale + pb * lo.vsblk, lo.vsblk & on);
+    const auto vzr = span_rsrc((const char*)a.v_zero + pb * lo.vsblk, lo.vsblk & on);
+    const uint32_t ko = pin(lo.k);
 #pragma unroll
-    for (int m = 0; m < D / 32; ++m) br.k[m] = *(const u4*)(kc + 32 * m + 8 * qd);
+    for (int u = 0; u < D / 64; ++u) br.k[u] = buf_load<u4>(kr, ko + 64 * u);
+    if constexpr (D == 128) {
+      br.v = buf_load<u4>(vr, lo.v);
+      br.vs = buf_load<u2>(vsr, lo.vs);
+      br.vz = buf_load<u2>(vzr, lo.vs);
+    } else {
+      const u2 t = buf_load<u2>(vr, lo.v);
+      br.v = u4{t.x, t.y, 0u, 0u};
+      br.vs = u2{buf_load<uint32_t>(vsr, lo.vs), 0u};
+      br.vz = u2{buf_load<uint32_t>(vzr, lo.vs), 0u};
+    }
+    br.ks = buf_load<uint16_t>(ksr, lo.ks);
+  } else {
+    const auto kr = span_rsrc((const char*)a.k_cache + pb * lo.kblk, lo.kblk & on);
+    const auto vr = span_rsrc((const char*)a.v_cache + pb * lo.vblk, lo.vblk & on);
+    const uint32_t ko = pin(lo.k), vo = pin(lo.v);
 #pragma unroll
-    for (int m = 0; m < D / 32; ++m) br.v[m] = *(const u4*)(vc + 32 * m + 8 * qd);
+    for (int m = 0; m < D / 32; ++m) br.k[m] = buf_load<u4>(kr, ko + 64 * m);
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) br.v[m] = buf_load<u4>(vr, vo + 64 * m);
   }
 }
 
@@ -196,13 +254,15 @@ void attn_partition_kernel(const AttnArgs a) {
   // j of a 64-entry chunk of the run, picked out later with readlane, so no
   // table load sits between the K/V loads of consecutive blocks.  Nothing
   // waits on another wave before the first K/V loads.
-  const int32_t* bt = a.block_tables + (int64_t)b * a.max_blocks;
+  // the sequence's table row; entries past max_blocks read as 0 (never used)
+  const auto btr = span_rsrc(a.block_tables + (int64_t)b * a.max_blocks,
+                             (uint32_t)a.max_blocks * 4u);
   const int bb = p * a.part_blocks;
   int per = (a.part_blocks + NW - 1) / NW;
   int tbl_next;
   {
     const int e = bb + w * per + lane;
-    tbl_next = lane < per && e < a.max_blocks ? bt[e] : 0;
+    tbl_next = lane < per ? buf_load<int>(btr, (uint32_t)e * 4u) : 0;
   }
   constexpr int QCW = RT * (D / 8);                         // 16-byte query chunks per wave
   constexpr int QPL = (QCW + kWave - 1) / kWave;            // per lane
@@ -234,7 +294,7 @@ void attn_partition_kernel(const AttnArgs a) {
   if (be - bb > a.part_blocks) {        // a last partition longer than the others
     per = (be - bb + NW - 1) / NW;      // (length past the grid): runs resized
     const int e = bb + w * per + lane;
-    tbl_next = lane < per && e < a.max_blocks ? bt[e] : 0;
+    tbl_next = lane < per ? buf_load<int>(btr, (uint32_t)e * 4u) : 0;
   }
   const int w0 = bb + w * per;                              // first block of this wave's run
   const int nmine = max(0, min(per, be - w0));
@@ -249,17 +309,19 @@ void attn_partition_kernel(const AttnArgs a) {
   int tblv = tbl_next;
   if (64 < nmine) {
     const int kk = 64 + lane;
-    tbl_next = kk < nmine ? bt[w0 + kk] : 0;
+    tbl_next = kk < nmine ? buf_load<int>(btr, (uint32_t)(w0 + kk) * 4u) : 0;
   }
-  auto fetch = [&](int j, BlockRegs<KV, D>& br) -> bool {
-    const int pb = __builtin_amdgcn_readlane(tblv, j);
-    const bool ok = pb >= 0 && (int64_t)pb < a.num_blocks;
-    load_block<KV, D>(a, ok ? pb : 0, g, rho, qd, br);
+  const LaneOffsets<KV, D> loff(a.num_kv_heads, g, rho, qd);
+  // block j of the current chunk of `cnt`; returns whether it holds data
+  // (j < cnt and its table entry names a pool block)
+  auto fetch = [&](int j, int cnt, BlockRegs<KV, D>& br) -> bool {
+    const int pb = __builtin_amdgcn_readlane(tblv, j & 63);
+    const bool ok = j < cnt && pb >= 0 && (int64_t)pb < a.num_blocks;
+    load_block<KV, D>(a, ok ? pb : 0, ok, loff, br);
     return ok;
   };
   BlockRegs<KV, D> r0, r1;
-  bool ok0 = false, ok1 = false;
-  if (nmine > 0) ok0 = fetch(0, r0);
+  bool ok0 = fetch(0, min(64, nmine), r0), ok1 = false;
 
   // ---- stage the query rows in this wave's own LDS area
   uint16_t* qw = q_s + w * RT * QSTR;
@@ -437,34 +499,25 @@ void attn_partition_kernel(const AttnArgs a) {
   };
 
   // ---- block loop, in chunks of 64 of this wave's blocks.  Two register
-  // sets: in the steady state the next block's loads are always issued before
-  // the current block is consumed, with no branch between them, so the wait
-  // before each block covers only that block's loads.
+  // sets: the next block's loads are always issued before the current block
+  // is consumed, with no branch between them, so the wait before each block
+  // covers only that block's loads.  A fetch past the chunk is a no-op load.
   for (int c0 = 0; c0 < nmine; c0 += 64) {
     const int cnt = min(64, nmine - c0);
     if (c0 > 0) {
       tblv = tbl_next;
       if (c0 + 64 < nmine) {                          // next chunk, one chunk ahead
         const int kk = c0 + 64 + lane;
-        tbl_next = kk < nmine ? bt[w0 + kk] : 0;
+        tbl_next = kk < nmine ? buf_load<int>(btr, (uint32_t)(w0 + kk) * 4u) : 0;
       }
-      ok0 = fetch(0, r0);
+      ok0 = fetch(0, cnt, r0);
     }
     const int i0 = w0 + c0;
-    int k = 0;
-    for (int pr = (cnt - 1) >> 1; pr > 0; --pr) {     // branch-free pairs of blocks
-      ok1 = fetch(k + 1, r1);
+    for (int k = 0; k < cnt; k += 2) {
+      ok1 = fetch(k + 1, cnt, r1);
       process(i0 + k, ok0, r0);
-      ok0 = fetch(k + 2, r0);
-      process(i0 + k + 1, ok1, r1);
-      k += 2;
-    }
-    if (k + 1 < cnt) {                                // two blocks left
-      ok1 = fetch(k + 1, r1);
-      process(i0 + k, ok0, r0);
-      process(i0 + k + 1, ok1, r1);
-    } else {                                          // one block left
-      process(i0 + k, ok0, r0);
+      ok0 = fetch(k + 2, cnt, r0);
+      if (k + 1 < cnt) process(i0 + k + 1, ok1, r1);
     }
   }
 
