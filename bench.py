@@ -2,13 +2,16 @@
 """Paged-decode benchmark on one MI355X.
 
 Headline workload: single-user long-context split-KV decode.  One step is one
-decoded token through 32 layers; per layer it writes the new token's K/V into
-that layer's block-paged cache (kv_cache_write) and runs split-KV paged
-attention over the 32768-token context (partition 512: partition kernel, then
-a log-sum-exp merge kernel).  Batch 1, q_len 1, 32 query / 8 KV heads, head_dim 128, fp16,
-2048 blocks of 16 per layer in a randomly permuted pool, one block table shared
-by the layers.  32 distinct layer caches (4 GiB) keep the working set far
-beyond the 256 MB Infinity Cache.
+decoded token through 32 layers; per layer, one append-form split-KV call
+stores the new token's K/V into that layer's block-paged cache and attends
+over the 32768-token context (partition 512: the partition kernel, which also
+does the store, then the log-sum-exp merge kernel).  Batch 1, q_len 1, 32
+query / 8 KV heads, head_dim 128, fp16, 2048 blocks of 16 per layer in a
+randomly permuted pool, one block table shared by the layers.  32 distinct
+layer caches (4 GiB) keep the working set far beyond the 256 MB Infinity
+Cache.  The step's 64 launches are captured once in a HIP graph and replayed,
+as a decode loop runs them; the same step launched eagerly, and the unfused
+two-call step (kv_cache_write, then split-KV decode), are reported beside it.
 
 value = KV bytes streamed per step (32 x 128 MiB) / step time, with all inputs
 resident in HBM.  The dominant kernel's roofline entry uses HIP events around
@@ -105,6 +108,17 @@ class Long32K:
         self.step_bytes = self.layer_bytes * layers
 
     def step(self):
+        """Per layer: store the new token and attend (append form)."""
+        P, c = self.P, self.case
+        for l in range(self.layers):
+            P.paged_attention_decode_splitkv_append(self.out[l], self.q[l], self.nk[l], self.nv[l],
+                                                    self.K[l], self.V[l], self.bt, self.cl,
+                                                    c.scale, c.gqa_factor, self.L,
+                                                    self.partition, self.ws)
+
+    def step_two_call(self):
+        """The same step as two calls per layer: kv_cache_write, then split-KV
+        decode over a length that includes the new token."""
         P, c = self.P, self.case
         for l in range(self.layers):
             P.kv_cache_write(self.nk[l], self.nv[l], self.K[l], self.V[l], self.slots)
@@ -114,23 +128,38 @@ class Long32K:
 
     def step_timed_kernels(self):
         """The same work as a step, reordered so that the 32 partition-kernel
-        launches run back to back between two events: all writes first, then
-        the partition kernels (one workspace per layer), then the merges."""
+        launches run back to back between two events: the partition kernels
+        (append form, one workspace per layer), then the merges."""
         P, c, torch = self.P, self.case, self.torch
         if not hasattr(self, "wss"):
             self.wss = [torch.zeros_like(self.ws) for _ in range(self.layers)]
-        for l in range(self.layers):
-            P.kv_cache_write(self.nk[l], self.nv[l], self.K[l], self.V[l], self.slots)
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
         for l in range(self.layers):
-            P.paged_attention_decode_splitkv_partials(self.q[l], self.K[l], self.V[l], self.bt,
-                                                      self.cl, c.scale, c.gqa_factor, self.L,
-                                                      self.partition, self.wss[l])
+            P.paged_attention_decode_splitkv_append_partials(
+                self.q[l], self.nk[l], self.nv[l], self.K[l], self.V[l], self.bt, self.cl,
+                c.scale, c.gqa_factor, self.L, self.partition, self.wss[l])
         e.record()
         for l in range(self.layers):
             P.paged_attention_decode_splitkv_merge(self.out[l], self.L, self.partition, self.wss[l])
         return s, e
+
+
+def graph_of(torch, fn):
+    """Capture one call of ``fn`` (a whole step's launches, stream-ordered on
+    the current stream) into a HIP graph.  Nothing is allocated or cleared by
+    the launches, so replays redo exactly the captured work."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
 
 
 def time_steps(torch, fn, steps, warmup):
@@ -272,22 +301,25 @@ def other_workload(name, P, W, torch, steps, warmup):
         V = [rnd(NB, 16, Hkv, D) for _ in range(layers)]
         per_tok_head = 4 * D
 
-        def step():
+        def step():             # append form: store the new rows and attend, one call
             for l in range(layers):
-                P.kv_cache_write(nk[l], nv[l], K[l], V[l], slots)
                 if part:
-                    P.paged_attention_decode_splitkv(out[l], q[l], K[l], V[l], bt, cl, scale, G,
-                                                     mcl, part, ws)
+                    P.paged_attention_decode_splitkv_append(out[l], q[l], nk[l], nv[l], K[l], V[l],
+                                                            bt, cl, scale, G, mcl, part, ws)
                 else:
-                    P.paged_attention_decode(out[l], q[l], K[l], V[l], bt, cl, scale, G)
-    ms = time_steps(torch, step, steps, warmup)
+                    P.paged_attention_decode_append(out[l], q[l], nk[l], nv[l], K[l], V[l], bt,
+                                                    cl, scale, G)
+    ms = time_steps(torch, graph_of(torch, step).replay, steps, warmup)
     layer_bytes = sum_len * Hkv * per_tok_head
     us = ms * 1e3 / layers
     return {"us_per_layer": round(us, 3), "kv_bytes_per_layer": layer_bytes,
             "kv_stream_gbs": round(layer_bytes / (us * 1e-6) / 1e9, 2),
             "pct_of_hbm_peak": round(100 * layer_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
             "decode_rows_per_s": round(B * Q / (ms * 1e-3), 1),
-            "layers": layers, "form": f"split-KV partition {part}" if part else "direct",
+            "layers": layers,
+            "form": (f"split-KV partition {part}" if part else "direct")
+            + (", quantize-on-write + decode" if name == "k8v4" else ", append form")
+            + ", HIP graph",
             "writes_per_layer": T, "kv_format": "k8v4" if name == "k8v4" else fmt}
 
 
@@ -324,9 +356,13 @@ def main():
     log("building the 32K workload")
     wl = Long32K(P, W, torch, args.layers, args.partition, args.seed)
     log("timing steps")
-    ms = time_steps(torch, wl.step, args.steps, args.warmup)
+    eager_ms = time_steps(torch, wl.step, args.steps, args.warmup)
+    graph = graph_of(torch, wl.step)
+    ms = time_steps(torch, graph.replay, args.steps, args.warmup)
+    two_call_ms = time_steps(torch, graph_of(torch, wl.step_two_call).replay, args.steps,
+                             args.warmup)
     gbs = wl.step_bytes / (ms * 1e-3) / 1e9
-    log(f"{ms:.3f} ms/step, {gbs:.1f} GB/s")
+    log(f"{ms:.3f} ms/step ({eager_ms:.3f} eager, {two_call_ms:.3f} two-call), {gbs:.1f} GB/s")
     kern_ms, launches = kernel_average_ms(torch, wl, args.steps)
     achieved = wl.layer_bytes / (kern_ms * 1e-3) / 1e9
     log(f"partition kernel {kern_ms * 1e3:.2f} us avg over {launches} launches, {achieved:.1f} GB/s")
@@ -347,13 +383,16 @@ def main():
         "config": {
             "workload": "long32k: single-user split-KV decode, batch 1, q_len 1, 32 query / 8 KV "
                         "heads, head_dim 128, fp16 K/V, context 32768 (2048 blocks of 16, "
-                        "permuted pool), 32 layers, partition 512; per layer one token write "
-                        "+ partition kernel + LSE merge kernel",
+                        "permuted pool), 32 layers, partition 512; per layer the new token's "
+                        "store + partition kernel + LSE merge kernel (append form), the "
+                        "step replayed as one HIP graph",
             "batch": 1, "context": wl.L, "layers": args.layers, "partition_size": args.partition,
             "kv_bytes_per_step": wl.step_bytes,
         },
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "us_per_layer": round(ms * 1e3 / args.layers, 3),
+        "eager_ms_per_step": round(eager_ms, 4),
+        "two_call_ms_per_step": round(two_call_ms, 4),
         "decode_tokens_per_s": round(1e3 / ms, 2),
         "roofline": {
             "bound": "hbm",

@@ -181,6 +181,54 @@ int paged_attention_decode_splitkv_merge(void* out, int out_dtype, int batch, in
                                          size_t workspace_bytes, void* stream);
 
 /*
+ * paged_attention_decode_append / paged_attention_decode_splitkv_append —
+ * the decode step with the slot write folded into the attention launch
+ * (mlxcel "KV Cache", Attention Dispatch and In-Place Decode Writes: the new
+ * K/V row is written into the cache in place during decode).  The result, in
+ * `out` and in the caches, is that of
+ *     kv_cache_write(new_key, new_value, key_cache, value_cache, slots, ...)
+ * followed by paged_attention_decode[_splitkv](...) with the same arguments,
+ * where the slots are those the block tables give the new positions: token
+ * b * q_len + i of new_key / new_value goes to position
+ * context_lens[b] - q_len + i of sequence b, i.e. block
+ * block_tables[b][pos / 16], row pos % 16.
+ *   new_key, new_value: [batch * q_len, num_kv_heads, head_dim] of kv_dtype
+ *   key_cache, value_cache: written (the new rows) and read
+ * A new token whose position is negative (context_lens[b] < q_len) or whose
+ * table entry lies outside [0, num_blocks) is neither stored nor attended.
+ * Lengths are clamped to max_blocks_per_seq * 16 first.  Every other argument,
+ * the workspace and the errors are those of the unfused calls.  The attention
+ * reads the new rows from new_key / new_value, so the launch never reads back
+ * what it stores.  Only 16-bit caches (f16, bf16).
+ */
+int paged_attention_decode_append(void* out, int out_dtype, const void* query,
+                                  const void* new_key, const void* new_value, void* key_cache,
+                                  void* value_cache, int kv_dtype, const int32_t* block_tables,
+                                  int max_blocks_per_seq, const int32_t* context_lens, int batch,
+                                  int q_len, int num_q_heads, int gqa_factor, int head_dim,
+                                  int block_size, int64_t num_blocks, float scale, void* stream);
+
+int paged_attention_decode_splitkv_append(void* out, int out_dtype, const void* query,
+                                          const void* new_key, const void* new_value,
+                                          void* key_cache, void* value_cache, int kv_dtype,
+                                          const int32_t* block_tables, int max_blocks_per_seq,
+                                          const int32_t* context_lens, int batch, int q_len,
+                                          int num_q_heads, int gqa_factor, int head_dim,
+                                          int block_size, int64_t num_blocks, float scale,
+                                          int max_context_len, int partition_size,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Partition-kernel half of paged_attention_decode_splitkv_append (the new
+ * rows are stored and their partial is in the workspace when it completes;
+ * finish with paged_attention_decode_splitkv_merge). */
+int paged_attention_decode_splitkv_append_partials(
+    const void* query, const void* new_key, const void* new_value, void* key_cache,
+    void* value_cache, int kv_dtype, const int32_t* block_tables, int max_blocks_per_seq,
+    const int32_t* context_lens, int batch, int q_len, int num_q_heads, int gqa_factor,
+    int head_dim, int block_size, int64_t num_blocks, float scale, int max_context_len,
+    int partition_size, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * kv_cache_write_k8v4 — quantize-on-write into a K8/V4 cache.
  *   key, value: [num_tokens, num_kv_heads, head_dim] of in_dtype (f16 or bf16)
  *   k_cache int8   [num_blocks, block_size, num_kv_heads, head_dim]

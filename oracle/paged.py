@@ -225,6 +225,53 @@ def _attend(qv, read_rows, num_blocks, hkv, block_tables, context_lens, scale,
 
 
 # ---------------------------------------------------------------------------
+# The decode step as one call: write the new rows where the tables put them,
+# then attend
+# ---------------------------------------------------------------------------
+
+def append_slots(block_tables, context_lens, q_len, num_blocks, block_size=BLOCK_SIZE):
+    """Cache slot of each new token, from the block tables.
+
+    Token ``i`` of sequence ``b`` is the one at position ``L_b - q_len + i``
+    (the length counts this step's tokens: "How MTPLX Manages Memory Using
+    Request-Sized Paged KV Cache", Request-Sized Offset Tracking), which lives
+    in table entry ``pos // block_size`` at row ``pos % block_size`` ("The KV
+    Cache", layout paragraph).  Returns int64 ``[B * q_len]`` in ``[b][i]``
+    order, -1 where the position is negative or its table entry names no pool
+    block (reading: such a token is neither stored nor attended).  ``L_b`` is
+    first clamped like every length (``effective_length``).
+    """
+    bt = np.asarray(block_tables)
+    out = np.full(len(context_lens) * q_len, -1, dtype=np.int64)
+    for b in range(len(context_lens)):
+        length = effective_length(int(context_lens[b]), bt.shape[1], block_size)
+        for i in range(q_len):
+            pos = length - q_len + i
+            if pos < 0:
+                continue
+            blk = int(bt[b, pos // block_size])
+            if 0 <= blk < num_blocks:
+                out[b * q_len + i] = blk * block_size + pos % block_size
+    return out
+
+
+def decode_append(query, new_key, new_value, key_cache, value_cache, block_tables,
+                  context_lens, scale, gqa_factor, fmt, block_size=BLOCK_SIZE):
+    """One decode step: store the new rows at their table slots, then attend
+    over the updated caches (mlxcel "KV Cache", Attention Dispatch and In-Place
+    Decode Writes: the new row goes into the cache in place during decode).
+
+    Returns ``(out float64 [B, Q, Hq, D], key_cache', value_cache')``.
+    """
+    q_len = np.asarray(query).shape[1]
+    slots = append_slots(block_tables, context_lens, q_len, key_cache.shape[0], block_size)
+    kc, vc = kv_cache_write(new_key, new_value, key_cache, value_cache, slots, block_size)
+    out = paged_attention(query, kc, vc, block_tables, context_lens, scale, gqa_factor, fmt,
+                          block_size=block_size)
+    return out, kc, vc
+
+
+# ---------------------------------------------------------------------------
 # Split-KV partition + log-sum-exp merge (used by the tests to show that the
 # partitioned form reaches the plain result)
 # ---------------------------------------------------------------------------

@@ -2,7 +2,8 @@
 
 Hand-written HIP kernels behind a C ABI (``include/pagedkv.h``): the
 reshape_and_cache slot scatter, paged-attention decode (direct and split-KV with
-a log-sum-exp merge) and their K8/V4-quantized variants.
+a log-sum-exp merge), the two fused into one launch (append form) and the
+K8/V4-quantized variants.
 
 The binding (``_binding``) loads ``libpagedkv.so`` on first use of any of the
 names below and raises ImportError if the library has not been built; there is
@@ -16,7 +17,8 @@ _EXPORTS = (
     "paged_attention_decode_k8v4", "paged_attention_decode_splitkv",
     "paged_attention_decode_splitkv_k8v4", "splitkv_workspace_size", "version",
     "paged_attention_decode_splitkv_partials", "paged_attention_decode_splitkv_k8v4_partials",
-    "paged_attention_decode_splitkv_merge",
+    "paged_attention_decode_splitkv_merge", "paged_attention_decode_append",
+    "paged_attention_decode_splitkv_append", "paged_attention_decode_splitkv_append_partials",
 )
 
 __all__ = list(_EXPORTS)

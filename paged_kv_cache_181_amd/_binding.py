@@ -61,6 +61,11 @@ SIGNATURES = {
     "paged_attention_decode_splitkv_partials": (_ATTN[2:] + [_i, _i, _p, _sz, _p], _i),
     "paged_attention_decode_splitkv_k8v4_partials": (_ATTN_K8V4[2:] + [_i, _i, _p, _sz, _p], _i),
     "paged_attention_decode_splitkv_merge": ([_p, _i, _i, _i, _i, _i, _i, _i, _p, _sz, _p], _i),
+    "paged_attention_decode_append": (_ATTN[:3] + [_p, _p] + _ATTN[3:] + [_p], _i),
+    "paged_attention_decode_splitkv_append": (_ATTN[:3] + [_p, _p] + _ATTN[3:]
+                                              + [_i, _i, _p, _sz, _p], _i),
+    "paged_attention_decode_splitkv_append_partials": ([_p, _p, _p] + _ATTN[3:]
+                                                       + [_i, _i, _p, _sz, _p], _i),
 }
 for _name, (_args, _res) in SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -215,6 +220,62 @@ def paged_attention_decode_splitkv(out, query, key_cache, value_cache, block_tab
         _dtype_code(key_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
         B, Q, Hq, gqa_factor, D, key_cache.shape[1], key_cache.shape[0], float(scale),
         int(max_context_len), int(partition_size), _ptr(workspace), nbytes, _stream(dev)))
+
+
+def _append_args(out, query, new_key, new_value, key_cache, value_cache, block_tables,
+                 context_lens, gqa_factor):
+    B, Q, Hq, D = _attn_common(out, query, block_tables, context_lens, gqa_factor)
+    _expect(key_cache.shape == value_cache.shape and key_cache.shape[2:] == (Hq // gqa_factor, D),
+            "caches must be [NB, 16, Hq/G, D]")
+    _expect(new_key.shape == new_value.shape == (B * Q, Hq // gqa_factor, D),
+            "new_key / new_value must be [B*q_len, Hq/G, D]")
+    _expect(query.dtype == key_cache.dtype == value_cache.dtype == new_key.dtype == new_value.dtype,
+            "query/new rows/cache dtype mismatch")
+    return [_ptr(out), _dtype_code(out), _ptr(query), _ptr(new_key), _ptr(new_value),
+            _ptr(key_cache), _ptr(value_cache), _dtype_code(key_cache), _ptr(block_tables),
+            block_tables.shape[1], _ptr(context_lens), B, Q, Hq, gqa_factor, D,
+            key_cache.shape[1], key_cache.shape[0]]
+
+
+def paged_attention_decode_append(out, query, new_key, new_value, key_cache, value_cache,
+                                  block_tables, context_lens, scale, gqa_factor):
+    """Slot write of the new rows (at the positions the tables give them) and
+    direct decode, in one launch."""
+    dev = _dev(out, query, new_key, new_value, key_cache, value_cache, block_tables, context_lens)
+    args = _append_args(out, query, new_key, new_value, key_cache, value_cache, block_tables,
+                        context_lens, gqa_factor)
+    _check(lib.paged_attention_decode_append(*args, float(scale), _stream(dev)))
+
+
+def paged_attention_decode_splitkv_append(out, query, new_key, new_value, key_cache, value_cache,
+                                          block_tables, context_lens, scale, gqa_factor,
+                                          max_context_len, partition_size, workspace):
+    """Slot write of the new rows and split-KV decode (partition kernel, then
+    the merge)."""
+    dev = _dev(out, query, new_key, new_value, key_cache, value_cache, block_tables, context_lens,
+               workspace)
+    args = _append_args(out, query, new_key, new_value, key_cache, value_cache, block_tables,
+                        context_lens, gqa_factor)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.paged_attention_decode_splitkv_append(
+        *args, float(scale), int(max_context_len), int(partition_size), _ptr(workspace), nbytes,
+        _stream(dev)))
+
+
+def paged_attention_decode_splitkv_append_partials(query, new_key, new_value, key_cache,
+                                                   value_cache, block_tables, context_lens, scale,
+                                                   gqa_factor, max_context_len, partition_size,
+                                                   workspace):
+    """Partition-kernel half of the append form (finish with
+    paged_attention_decode_splitkv_merge)."""
+    dev = _dev(query, new_key, new_value, key_cache, value_cache, block_tables, context_lens,
+               workspace)
+    args = _append_args(query, query, new_key, new_value, key_cache, value_cache, block_tables,
+                        context_lens, gqa_factor)        # (no output: query stands in for its shape)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.paged_attention_decode_splitkv_append_partials(
+        *args[2:], float(scale), int(max_context_len), int(partition_size), _ptr(workspace),
+        nbytes, _stream(dev)))
 
 
 def _k8v4_check(query, gqa_factor, k_cache, k_scale, v_cache, v_scale, v_zero):

@@ -279,8 +279,14 @@ void attn_partition_kernel(const AttnArgs a) {
   }
   int L = a.context_lens[b];
   L = min(max(L, 0), a.max_blocks * kBlock);
-  const int nblk = (L + kBlock - 1) / kBlock;
-  if (split && bb >= nblk) {                                // partition past this sequence:
+  // Append form: the q_len new tokens (positions L-Q .. L-1) come from the
+  // new K/V rows, not the cache; the partition holding position L-1 attends
+  // to them and stores them into the cache.  Cache blocks then cover Lc.
+  const bool append = KV != Fmt::K8V4 && a.new_k != nullptr;
+  const int Lc = append ? max(L - Q, 0) : L;                // positions read from the cache
+  const int nblk = (Lc + kBlock - 1) / kBlock;
+  const int p_new = append && L > 0 ? min((L - 1) / kBlock / a.part_blocks, a.num_parts - 1) : -1;
+  if (split && bb >= nblk && p != p_new) {                  // partition past this sequence:
     // mark it empty (max -inf, sum 0) so the merge can read every partition
     // without first reading the sequence length
     for (int rr = threadIdx.x; rr < GQ; rr += NW * kWave) {
@@ -306,22 +312,31 @@ void attn_partition_kernel(const AttnArgs a) {
   const int nvis = row_ok ? (L - Q + iq + 1) : L;           // visible positions of the row
   const int full_lim = L - Q + 1;                           // every row sees j < full_lim
 
+  // append form: the table entry of each new token's position (lane rho = token)
+  int tnew = -1;
+  if (p == p_new) {
+    const int pos = L - Q + rho;
+    if (rho < Q && pos >= 0) tnew = buf_load<int>(btr, (uint32_t)(pos / kBlock) * 4u);
+  }
+
   int tblv = tbl_next;
   if (64 < nmine) {
     const int kk = 64 + lane;
     tbl_next = kk < nmine ? buf_load<int>(btr, (uint32_t)(w0 + kk) * 4u) : 0;
   }
   const LaneOffsets<KV, D> loff(a.num_kv_heads, g, rho, qd);
-  // block j of the current chunk of `cnt`; returns whether it holds data
-  // (j < cnt and its table entry names a pool block)
-  auto fetch = [&](int j, int cnt, BlockRegs<KV, D>& br) -> bool {
+  // block j of the current chunk of `cnt` (first chunk block c0); returns
+  // the mask of its tokens that hold data: none if j >= cnt or its table
+  // entry names no pool block, else the tokens before the cache length
+  auto fetch = [&](int c0, int j, int cnt, BlockRegs<KV, D>& br) -> uint32_t {
     const int pb = __builtin_amdgcn_readlane(tblv, j & 63);
     const bool ok = j < cnt && pb >= 0 && (int64_t)pb < a.num_blocks;
     load_block<KV, D>(a, ok ? pb : 0, ok, loff, br);
-    return ok;
+    const int left = Lc - (w0 + c0 + j) * kBlock;           // cache tokens from this block on
+    return !ok ? 0u : left >= kBlock ? 0xffffu : (1u << max(left, 0)) - 1u;
   };
   BlockRegs<KV, D> r0, r1;
-  bool ok0 = fetch(0, min(64, nmine), r0), ok1 = false;
+  uint32_t ok0 = fetch(0, 0, min(64, nmine), r0), ok1 = 0u;
 
   // ---- stage the query rows in this wave's own LDS area
   uint16_t* qw = q_s + w * RT * QSTR;
@@ -349,11 +364,12 @@ void attn_partition_kernel(const AttnArgs a) {
 
   const float sl2 = a.scale_log2;
 
-  auto process = [&](int i, bool ok, BlockRegs<KV, D>& br) {
-    const int j0 = i * kBlock;
-    const bool tail = !ok || j0 + kBlock > L;                // some tokens past the length
-    const bool full = ok && j0 + kBlock <= full_lim;         // no masking needed at all
-    const bool tok_ok = ok && j0 + rho < L;                  // this lane's token (rho) exists
+  // One tile of 16 tokens at positions j0 .. j0+15; bit t of vmask says
+  // whether token t holds data (wave-uniform).
+  auto process = [&](int j0, uint32_t vmask, BlockRegs<KV, D>& br) {
+    const bool tail = vmask != 0xffffu;                      // some tokens hold no data
+    const bool full = !tail && j0 + kBlock <= full_lim;      // no masking needed at all
+    const bool tok_ok = (vmask >> rho) & 1u;                 // this lane's token (rho) exists
 
     // ---- stage V in load-lane order: the 16-byte chunk (m, c) of token t at
     // m*1024 + (16c + t)*16, i.e. lane (t, c) of load m writes where it read.
@@ -439,7 +455,7 @@ void attn_partition_kernel(const AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = j0 + 4 * qd + r;
-        if (!ok || j >= nvis) sv[r] = kNegInf;
+        if (!((vmask >> (4 * qd + r)) & 1u) || j >= nvis) sv[r] = kNegInf;
       }
     }
     const float mx = quarter_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
@@ -510,14 +526,45 @@ void attn_partition_kernel(const AttnArgs a) {
         const int kk = c0 + 64 + lane;
         tbl_next = kk < nmine ? buf_load<int>(btr, (uint32_t)(w0 + kk) * 4u) : 0;
       }
-      ok0 = fetch(0, cnt, r0);
+      ok0 = fetch(c0, 0, cnt, r0);
     }
-    const int i0 = w0 + c0;
+    const int j0 = (w0 + c0) * kBlock;
     for (int k = 0; k < cnt; k += 2) {
-      ok1 = fetch(k + 1, cnt, r1);
-      process(i0 + k, ok0, r0);
-      ok0 = fetch(k + 2, cnt, r0);
-      if (k + 1 < cnt) process(i0 + k + 1, ok1, r1);
+      ok1 = fetch(c0, k + 1, cnt, r1);
+      process(j0 + k * kBlock, ok0, r0);
+      ok0 = fetch(c0, k + 2, cnt, r0);
+      if (k + 1 < cnt) process(j0 + (k + 1) * kBlock, ok1, r1);
+    }
+  }
+
+  // ---- append form: the last wave of the partition holding position L-1
+  // takes the new tokens as one more tile (token t at position L-Q+t, rows
+  // past q_len read as zeros) and stores them into their cache slots.
+  if constexpr (KV != Fmt::K8V4) {
+    if (p == p_new && w == NW - 1) {
+      BlockRegs<KV, D> rn;
+      const uint32_t rows_b = (uint32_t)(Q * a.num_kv_heads * D * 2);
+      const int64_t first = (int64_t)b * Q * a.num_kv_heads * D * 2;
+      const auto kr = span_rsrc((const char*)a.new_k + first, rows_b);
+      const auto vr = span_rsrc((const char*)a.new_v + first, rows_b);
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m) rn.k[m] = buf_load<u4>(kr, loff.k + 64 * m);
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m) rn.v[m] = buf_load<u4>(vr, loff.v + 64 * m);
+      const bool tv = tnew >= 0 && (int64_t)tnew < a.num_blocks;   // rho < Q, position >= 0
+      const uint32_t vmask = (uint32_t)__builtin_amdgcn_ballot_w64(tv && qd == 0) & 0xffffu;
+      if (tv) {
+        const int pos = L - Q + rho;
+        const int64_t row = ((int64_t)tnew * kBlock + (pos & (kBlock - 1))) * a.num_kv_heads + g;
+        char* kd = (char*)a.k_cache + row * (D * 2) + 16 * qd;
+        char* vd = (char*)a.v_cache + row * (D * 2) + 16 * qd;
+#pragma unroll
+        for (int m = 0; m < D / 32; ++m) {
+          *(u4*)(kd + 64 * m) = rn.k[m];
+          *(u4*)(vd + 64 * m) = rn.v[m];
+        }
+      }
+      process(L - Q, vmask, rn);
     }
   }
 
@@ -607,12 +654,16 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool use = p0 + u * NG < np && mp[u] != kNegInf;   // -inf: partition saw nothing
+      // -inf: the partition saw nothing and its o was never written (it may
+      // hold anything, NaN included), so it is selected away, not weighted by 0
+      const bool use = p0 + u * NG < np && mp[u] != kNegInf;
       const float m_new = use ? fmaxf(m_t, mp[u]) : m_t;
-      const float e_old = (!use || m_t == kNegInf) ? (use ? 0.f : 1.f) : fast_exp2(m_t - m_new);
-      const float e_new = use ? fast_exp2(mp[u] - m_new) : 0.f;
-      acc = acc * e_old + op[u] * e_new;
-      den = den * e_old + lp[u] * e_new;
+      const float e_old = m_t == kNegInf ? 0.f : fast_exp2(m_t - m_new);
+      const float e_new = fast_exp2(mp[u] - m_new);
+      if (use) {
+        acc = acc * e_old + op[u] * e_new;
+        den = den * e_old + lp[u] * e_new;
+      }
       m_t = m_new;
     }
   }

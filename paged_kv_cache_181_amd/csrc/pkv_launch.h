@@ -36,6 +36,8 @@ struct AttnArgs {
   float* ws_o;                   // split form: [B*Q*Hq, P, D] unnormalised partial outputs
   float* ws_m;                   // split form: [B*Q*Hq, P] running max (log2 units)
   float* ws_l;                   // split form: [B*Q*Hq, P] softmax denominators
+  const void* new_k;             // append form (16-bit only): [B*Q, Hkv, D] new rows, else NULL
+  const void* new_v;             // append form: [B*Q, Hkv, D]
 };
 
 // kv_fmt: 0 f16, 1 bf16, 3 k8v4; q_fmt: 0 f16, 1 bf16 (must equal kv_fmt unless k8v4).

@@ -51,7 +51,9 @@ def run_decode(P, dc: DevCase, *, split: bool, partition_size=512, out_dtype=tor
         mcl = int(cl.max().item()) if max_context_len is None else max_context_len
         nbytes = P.splitkv_workspace_size(q.shape[0], q.shape[1], q.shape[2], q.shape[3], mcl,
                                           partition_size)
-        ws = torch.zeros(max(nbytes, 16) // 4 + 4, dtype=torch.float32, device=q.device)
+        # the contents on entry must not matter: start from NaN
+        ws = torch.full((max(nbytes, 16) // 4 + 4,), float("nan"), dtype=torch.float32,
+                        device=q.device)
         P.paged_attention_decode_splitkv(out, q, k, v, bt, cl, c.scale, c.gqa_factor, mcl,
                                          partition_size, ws)
     else:

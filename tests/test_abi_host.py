@@ -164,3 +164,25 @@ def test_k8v4_attention_argument_errors(P):
     bad[5] = None
     assert lib.paged_attention_decode_k8v4(*bad, None) == -1
     assert lib.paged_attention_decode_splitkv_k8v4(*base, 64, 512, None, 0, None) == -4
+
+
+def test_append_argument_errors(P):
+    lib = P.lib
+    # out, out_dtype, query, new_key, new_value, k, v, kv_dtype, bt, mb, cl, B, Q, Hq, G, D, bs, nb, scale
+    base = [FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 4, FAKE, 2, 1, 32, 4, 128, 16, 64, 0.1]
+    bad = list(base)
+    bad[3] = None
+    assert lib.paged_attention_decode_append(*bad, None) == -1
+    bad = list(base)
+    bad[4] = ctypes.c_void_p(4104)
+    assert lib.paged_attention_decode_append(*bad, None) == -6
+    bad = list(base)
+    bad[7] = 3                                        # no K8/V4 append form
+    assert lib.paged_attention_decode_append(*bad, None) == -3
+    assert lib.paged_attention_decode_splitkv_append(*base, 64, 512, None, 0, None) == -4
+    assert lib.paged_attention_decode_splitkv_append(*base, 64, 40, FAKE, 1 << 30, None) == -3
+    zero = list(base)
+    zero[11] = 0
+    for i in (0, 2, 3, 4, 5, 6, 8, 10):
+        zero[i] = None
+    assert lib.paged_attention_decode_append(*zero, None) == 0

@@ -314,7 +314,7 @@ def test_k8v4_decode_matches_oracle_on_the_same_codes(P, full, split):
         if split:
             mcl = int(case.context_lens.max())
             n = P.splitkv_workspace_size(*q.shape[:3], q.shape[3], mcl, 512)
-            ws = torch.zeros(n // 4 + 4, dtype=torch.float32, device="cuda")
+            ws = torch.full((n // 4 + 4,), float("nan"), dtype=torch.float32, device="cuda")
             P.paged_attention_decode_splitkv_k8v4(out, q, *args, mcl, 512, ws)
         else:
             P.paged_attention_decode_k8v4(out, q, *args)
@@ -361,7 +361,7 @@ def test_workspace_reuse_and_two_launch_path(P):
     B, Q, Hq, D = dc.q.shape
     mcl = int(case.context_lens.max())
     n = P.splitkv_workspace_size(B, Q, Hq, D, mcl, 512)
-    ws = torch.zeros(n // 4, dtype=torch.float32, device="cuda")
+    ws = torch.full((n // 4,), float("nan"), dtype=torch.float32, device="cuda")
     ws2 = torch.zeros_like(ws)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(5)
@@ -376,3 +376,181 @@ def test_workspace_reuse_and_two_launch_path(P):
         P.paged_attention_decode_splitkv_merge(two, mcl, 512, ws2)
         torch.cuda.synchronize()
         assert torch.equal(fused, two), it
+
+
+# ------------------------------------------------------------------ append form
+#
+# paged_attention_decode[_splitkv]_append stores the new rows at the slots the
+# tables give them and attends in the same launch; the oracle does the same in
+# two plain steps (write, then attend over the written caches).
+
+APPEND_CASES = {
+    "tiny": lambda: W.tiny(),
+    "small_f16_d64": lambda: small(101),
+    "small_bf16_d128_g4": lambda: small(102, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                                        fmt="bf16"),
+    "small_verify_q4": lambda: small(103, q_len=4, num_q_heads=16, num_kv_heads=4, head_dim=128),
+    "small_g8_q2": lambda: small(104, q_len=2, num_q_heads=16, num_kv_heads=2, head_dim=64,
+                                 fmt="bf16"),
+    "edge_lengths": lambda: small(107, batch=8, q_len=2, num_q_heads=8, num_kv_heads=2,
+                                  head_dim=128, lengths=[0, 1, 2, 15, 16, 17, 32, 33]),
+    "partition_edges": lambda: small(120, batch=7, q_len=1, num_q_heads=32, num_kv_heads=8,
+                                     head_dim=128, lengths=[513, 512, 33, 32, 1, 16, 545]),
+    "partition_edges_q4": lambda: small(121, batch=6, q_len=4, num_q_heads=16, num_kv_heads=4,
+                                        head_dim=64, fmt="bf16",
+                                        lengths=[515, 512, 36, 32, 4, 3]),
+    "llama8b_batch": lambda: W.llama8b_batch(),
+    "spec_verify_b8": lambda: W.spec_verify(batch=8),
+    "long32k": lambda: W.long32k(),
+}
+
+_append_cache = {}
+
+
+def get_append_case(name):
+    if name not in _append_cache:
+        case = APPEND_CASES[name]()
+        _append_cache[name] = (case, oracle.decode_append(
+            case.query, case.new_key, case.new_value, case.key_cache, case.value_cache,
+            case.block_tables, case.context_lens, case.scale, case.gqa_factor, case.fmt))
+    return _append_cache[name]
+
+
+def run_append(P, dc, *, split, psize=512, out_dtype=torch.float32, bt=None, mcl=None):
+    """Fresh copies of the caches, then one append-form call; returns
+    (out, key_cache, value_cache)."""
+    c = dc.case
+    k, v = dc.k.clone(), dc.v.clone()
+    bt = dc.bt if bt is None else bt
+    out = torch.full(dc.q.shape, float("nan"), dtype=out_dtype, device="cuda")
+    if split:
+        mcl = int(dc.cl.max().item()) if mcl is None else mcl
+        B, Q, Hq, D = dc.q.shape
+        n = P.splitkv_workspace_size(B, Q, Hq, D, mcl, psize)
+        ws = torch.full((max(n, 16) // 4 + 4,), float("nan"), dtype=torch.float32, device="cuda")
+        P.paged_attention_decode_splitkv_append(out, dc.q, dc.new_k, dc.new_v, k, v, bt, dc.cl,
+                                                c.scale, c.gqa_factor, mcl, psize, ws)
+    else:
+        P.paged_attention_decode_append(out, dc.q, dc.new_k, dc.new_v, k, v, bt, dc.cl, c.scale,
+                                        c.gqa_factor)
+    torch.cuda.synchronize()
+    return out, k, v
+
+
+@pytest.mark.parametrize("name", list(APPEND_CASES))
+@pytest.mark.parametrize("split,psize", [(False, 0), (True, 512), (True, 32)])
+def test_append_matches_write_then_attend(P, name, split, psize):
+    case, (ref, kc, vc) = get_append_case(name)
+    if case.name == "long32k" and not split:
+        pytest.skip("the 32K single sequence is a split-KV workload")
+    dc = DevCase(case)
+    out, k, v = run_append(P, dc, split=split, psize=psize or 512)
+    assert np.array_equal(dev_to_bits(k), kc), "key cache after the append differs"
+    assert np.array_equal(dev_to_bits(v), vc), "value cache after the append differs"
+    err = max_err(out, ref)
+    assert err <= 2e-4, f"{name}: fp32-out max abs err {err}"
+    out16, _, _ = run_append(P, dc, split=split, psize=psize or 512, out_dtype=dc.q.dtype)
+    assert torch.equal(out16, out.to(dc.q.dtype))
+
+
+def test_append_long32k_bench_launch_configuration(P):
+    """The 32K decode step as the bench times it: split-KV append, partition
+    512, fp16 output."""
+    case, (ref, kc, vc) = get_append_case("long32k")
+    dc = DevCase(case)
+    out, k, v = run_append(P, dc, split=True, psize=512, out_dtype=torch.float16)
+    assert max_err(out, ref) <= TOL
+    assert np.array_equal(dev_to_bits(k), kc) and np.array_equal(dev_to_bits(v), vc)
+
+
+def test_append_agrees_with_the_two_call_step(P):
+    """Same step through kv_cache_write + paged_attention_decode_splitkv: same
+    caches bit for bit, outputs equal up to fp32 summation order."""
+    case, _ = get_append_case("small_verify_q4")
+    dc = DevCase(case)
+    out_a, k_a, v_a = run_append(P, dc, split=True, psize=32)
+    k, v = dc.k.clone(), dc.v.clone()
+    P.kv_cache_write(dc.new_k, dc.new_v, k, v, dc.slots)
+    out_b = run_decode(P, dc, split=True, partition_size=32, k=k, v=v)
+    assert torch.equal(k, k_a) and torch.equal(v, v_a)
+    assert (out_a - out_b).abs().max().item() <= 1e-5
+
+
+def test_append_skips_new_tokens_without_a_pool_block(P):
+    """A new token whose table entry names no pool block is neither stored nor
+    attended (nor are the other positions of that entry)."""
+    case = small(122, batch=3, q_len=2, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                 lengths=[40, 33, 18])
+    case.block_tables[0, 2] = case.num_blocks + 4      # new positions 38, 39 of row 0
+    case.block_tables[1, 2] = -7                       # new position 32 of row 1 (33 -> 31, 32)
+    ref, kc, vc = oracle.decode_append(case.query, case.new_key, case.new_value, case.key_cache,
+                                       case.value_cache, case.block_tables, case.context_lens,
+                                       case.scale, case.gqa_factor, case.fmt)
+    dc = DevCase(case)
+    for split, psize in ((False, 512), (True, 16), (True, 32)):
+        out, k, v = run_append(P, dc, split=split, psize=psize)
+        assert np.array_equal(dev_to_bits(k), kc) and np.array_equal(dev_to_bits(v), vc)
+        assert max_err(out, ref) <= 2e-4
+
+
+def test_graph_replays_match_eager(P):
+    """The step captured in a HIP graph (write, split-KV decode, append form)
+    and replayed several times, with eager work and synchronisation between
+    replays: every replay equals the eager results bit for bit."""
+    case, _ = get_append_case("small_bf16_d128_g4")
+    dc = DevCase(case)
+    B, Q, Hq, D = dc.q.shape
+    mcl = int(case.context_lens.max())
+    n = P.splitkv_workspace_size(B, Q, Hq, D, mcl, 32)
+    k, v = dc.k.clone(), dc.v.clone()
+    ws1 = torch.zeros(n // 4, dtype=torch.float32, device="cuda")
+    ws2 = torch.zeros_like(ws1)
+    outs = [torch.zeros(dc.q.shape, dtype=torch.float32, device="cuda") for _ in range(2)]
+
+    def step():
+        P.kv_cache_write(dc.new_k, dc.new_v, k, v, dc.slots)
+        P.paged_attention_decode_splitkv(outs[0], dc.q, k, v, dc.bt, dc.cl, case.scale,
+                                         case.gqa_factor, mcl, 32, ws1)
+        P.paged_attention_decode_splitkv_append(outs[1], dc.q, dc.new_k, dc.new_v, k, v, dc.bt,
+                                                dc.cl, case.scale, case.gqa_factor, mcl, 32, ws2)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    k_eager, v_eager = k.clone(), v.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), f"replay {rep}"
+        assert torch.equal(k, k_eager) and torch.equal(v, v_eager)
+        run_decode(P, dc, split=False)                  # eager work between replays
+
+
+def test_append_partials_then_merge_equals_the_single_call(P):
+    case, _ = get_append_case("small_verify_q4")
+    dc = DevCase(case)
+    out_a, k_a, v_a = run_append(P, dc, split=True, psize=32)
+    B, Q, Hq, D = dc.q.shape
+    mcl = int(case.context_lens.max())
+    ws = torch.zeros(P.splitkv_workspace_size(B, Q, Hq, D, mcl, 32) // 4, dtype=torch.float32,
+                     device="cuda")
+    k, v = dc.k.clone(), dc.v.clone()
+    out_b = torch.empty_like(out_a)
+    P.paged_attention_decode_splitkv_append_partials(dc.q, dc.new_k, dc.new_v, k, v, dc.bt, dc.cl,
+                                                     case.scale, case.gqa_factor, mcl, 32, ws)
+    P.paged_attention_decode_splitkv_merge(out_b, mcl, 32, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a, out_b)
+    assert torch.equal(k, k_a) and torch.equal(v, v_a)

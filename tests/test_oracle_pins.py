@@ -342,6 +342,34 @@ def test_generator_slots_land_on_the_new_positions():
                 t += 1
 
 
+def test_append_slots_by_hand_and_against_the_generator():
+    # positions 15, 16, 17 of a row with table [5, 2]: block 5 row 15, then
+    # block 2 rows 0 and 1; a row shorter than q_len has no slot for its
+    # first tokens; an out-of-pool entry gives none either
+    table = np.array([[5, 2], [3, -1], [9, 1]], np.int32)
+    slots = oracle.append_slots(table, [18, 2, 16], 3, num_blocks=8)
+    assert slots.tolist() == [95, 32, 33, -1, 48, 49, -1, -1, -1]
+    # the generator assigns the new tokens' slots with its own bookkeeping
+    for case in (small_case(33, batch=4, q_len=4, lengths=[4, 20, 64, 37]), W.tiny(),
+                 W.spec_verify(batch=6, hi=600)):
+        got = oracle.append_slots(case.block_tables, case.context_lens, case.q_len,
+                                  case.num_blocks)
+        assert np.array_equal(got, case.slot_mapping)
+
+
+def test_decode_append_is_write_then_attend():
+    case = small_case(34, batch=3, q_len=2, lengths=[2, 17, 40])
+    out, kc, vc = oracle.decode_append(case.query, case.new_key, case.new_value, case.key_cache,
+                                       case.value_cache, case.block_tables, case.context_lens,
+                                       case.scale, case.gqa_factor, case.fmt)
+    kc2, vc2 = oracle.kv_cache_write(case.new_key, case.new_value, case.key_cache,
+                                     case.value_cache, case.slot_mapping)
+    assert np.array_equal(kc, kc2) and np.array_equal(vc, vc2)
+    import dataclasses
+    written = dataclasses.replace(case, key_cache=kc2, value_cache=vc2)
+    assert np.abs(out - sdpa_reference(written)).max() < 1e-12
+
+
 def test_cache_size_closed_form_matches_page():
     g = golden("kv_cache_arithmetic.json")
     per_tok = oracle.kv_cache_bytes_per_token(g["num_layers"], g["num_kv_heads"], g["head_dim"], "f16")
