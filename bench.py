@@ -247,12 +247,15 @@ OTHER = {
     "llama8b_batch": (2, 8, 512),
     "spec_verify": (4, 8, 512),
     "k8v4": (5, 8, 512),
+    "long32k_window2048": (3, 32, 128),
 }
+WINDOW = {"long32k_window2048": 2048}       # sliding window of the windowed workloads
 
 
 def other_workload(name, P, W, torch, steps, warmup):
     seed, layers, part = OTHER[name]
-    lay, B, Q, Hq, Hkv, D, fmt = W.layout_of(name, seed)
+    window = WINDOW.get(name, 0)
+    lay, B, Q, Hq, Hkv, D, fmt = W.layout_of(name.split("_window")[0], seed)
     dev = torch.device("cuda:0")
     dt = torch.float16 if fmt == "f16" else torch.bfloat16
     gen = torch.Generator(device=dev)
@@ -271,9 +274,12 @@ def other_workload(name, P, W, torch, steps, warmup):
     out = [torch.empty(B, Q, Hq, D, dtype=dt, device=dev) for _ in range(layers)]
     ws = None
     if part:
-        ws = torch.zeros(P.splitkv_workspace_size(B, Q, Hq, D, mcl, part) // 4 + 4,
+        span = min(mcl, window + Q + 15) if window else mcl   # a window's grid spans the window
+        ws = torch.zeros(P.splitkv_workspace_size(B, Q, Hq, D, span, part) // 4 + 4,
                          dtype=torch.float32, device=dev)
     sum_len = int(lay.context_lens.astype("int64").sum())
+    if window:          # positions any row sees (q_len 1: the last `window` of each sequence)
+        sum_len = int(sum(min(int(n), window + Q - 1) for n in lay.context_lens))
     if name == "k8v4":
         pools = []
         all_slots = torch.arange(NB * 16, dtype=torch.int64, device=dev)
@@ -303,7 +309,11 @@ def other_workload(name, P, W, torch, steps, warmup):
 
         def step():             # append form: store the new rows and attend, one call
             for l in range(layers):
-                if part:
+                if window:      # the windowed step: write, then windowed split-KV decode
+                    P.kv_cache_write(nk[l], nv[l], K[l], V[l], slots)
+                    P.paged_attention_decode_splitkv_window(out[l], q[l], K[l], V[l], bt, cl,
+                                                            scale, G, window, mcl, part, ws)
+                elif part:
                     P.paged_attention_decode_splitkv_append(out[l], q[l], nk[l], nv[l], K[l], V[l],
                                                             bt, cl, scale, G, mcl, part, ws)
                 else:
@@ -318,7 +328,8 @@ def other_workload(name, P, W, torch, steps, warmup):
             "decode_rows_per_s": round(B * Q / (ms * 1e-3), 1),
             "layers": layers,
             "form": (f"split-KV partition {part}" if part else "direct")
-            + (", quantize-on-write + decode" if name == "k8v4" else ", append form")
+            + (", quantize-on-write + decode" if name == "k8v4"
+               else f", write + sliding window {window}" if window else ", append form")
             + ", HIP graph",
             "writes_per_layer": T, "kv_format": "k8v4" if name == "k8v4" else fmt}
 
@@ -410,7 +421,7 @@ def main():
         del wl.K, wl.V
         torch.cuda.empty_cache()
         result["other_workloads"] = {}
-        for name in ("tiny", "llama8b_batch", "spec_verify", "k8v4"):
+        for name in ("tiny", "llama8b_batch", "spec_verify", "k8v4", "long32k_window2048"):
             log(f"timing {name}")
             result["other_workloads"][name] = other_workload(name, P, W, torch, args.steps,
                                                              args.warmup)

@@ -181,6 +181,43 @@ int paged_attention_decode_splitkv_merge(void* out, int out_dtype, int batch, in
                                          size_t workspace_bytes, void* stream);
 
 /*
+ * paged_attention_decode_window / paged_attention_decode_splitkv_window —
+ * decode over a sliding window of the context ("How MTPLX Manages Memory
+ * Using Request-Sized Paged KV Cache", Sliding-Window Memory Control and the
+ * sliding_window argument of its paged attention call: older tokens are
+ * masked while their blocks stay allocated; mlxcel "KV Cache",
+ * RotatingKVCache).  Query row i of sequence b, at position
+ * p = context_lens[b] - q_len + i, sees positions max(0, p - W + 1) .. p,
+ * i.e. its W most recent positions (itself included); W = sliding_window,
+ * 0 meaning the whole context.  Blocks that hold no position any row may see
+ * are not read.  In the split form the partitions of a sequence are counted
+ * from the block holding its first visible position, so the grid spans
+ * S = min(max_context_len, sliding_window + q_len + 15) positions and the
+ * workspace needs paged_attention_decode_splitkv_workspace_size(..., S,
+ * partition_size) bytes (partitions with nothing to read are marked empty).
+ * Every other argument and the errors are those of
+ * paged_attention_decode[_splitkv]; sliding_window < 0 returns PKV_ERR_SHAPE.
+ * 16-bit caches only.
+ */
+int paged_attention_decode_window(void* out, int out_dtype, const void* query,
+                                  const void* key_cache, const void* value_cache, int kv_dtype,
+                                  const int32_t* block_tables, int max_blocks_per_seq,
+                                  const int32_t* context_lens, int batch, int q_len,
+                                  int num_q_heads, int gqa_factor, int head_dim, int block_size,
+                                  int64_t num_blocks, float scale, int sliding_window,
+                                  void* stream);
+
+int paged_attention_decode_splitkv_window(void* out, int out_dtype, const void* query,
+                                          const void* key_cache, const void* value_cache,
+                                          int kv_dtype, const int32_t* block_tables,
+                                          int max_blocks_per_seq, const int32_t* context_lens,
+                                          int batch, int q_len, int num_q_heads, int gqa_factor,
+                                          int head_dim, int block_size, int64_t num_blocks,
+                                          float scale, int sliding_window, int max_context_len,
+                                          int partition_size, void* workspace,
+                                          size_t workspace_bytes, void* stream);
+
+/*
  * paged_attention_decode_append / paged_attention_decode_splitkv_append —
  * the decode step with the slot write folded into the attention launch
  * (mlxcel "KV Cache", Attention Dispatch and In-Place Decode Writes: the new

@@ -154,26 +154,45 @@ def visible_count(length: int, q_len: int, i: int) -> int:
     return length - q_len + i + 1
 
 
-def attend_rows(q, keys, vals, valid, scale, q_len):
+def window_start(length: int, q_len: int, i: int, window: int) -> int:
+    """First position query row ``i`` may see under a sliding window.
+
+    "How MTPLX Manages Memory Using Request-Sized Paged KV Cache",
+    Sliding-Window Memory Control: attention is trimmed to the most recent
+    ``window`` cached tokens, older ones are masked (their blocks stay
+    allocated); mlxcel "KV Cache", RotatingKVCache.  Reading for a block of
+    ``q_len`` rows: row ``i`` at position ``p = length - q_len + i`` sees its
+    own ``window`` most recent positions ``p - window + 1 .. p`` (so each
+    verify row still equals a single-token decode).  ``window <= 0`` means no
+    window.
+    """
+    if window <= 0:
+        return 0
+    return max(visible_count(length, q_len, i) - window, 0)
+
+
+def attend_rows(q, keys, vals, valid, scale, q_len, window=0):
     """Masked softmax attention for one (sequence, KV head).
 
     q: float64 ``[q_len, G, D]`` (the G query heads sharing this KV head);
     keys/vals: float64 ``[n_pos, D]``; valid: bool ``[n_pos]``.
     Returns float64 ``[q_len, G, D]``.  Rows that see no valid position
-    return zeros (reading: pages silent).
+    return zeros (reading: pages silent).  Row ``i`` sees positions
+    ``window_start .. visible_count - 1``.
     """
     ql, g, d = q.shape
     out = np.zeros((ql, g, d), dtype=np.float64)
     n_pos = keys.shape[0]
     for i in range(ql):
         n = min(visible_count(n_pos, q_len, i), n_pos)
-        if n <= 0:
+        lo = window_start(n_pos, q_len, i, window)
+        if n <= lo:
             continue
-        mask = valid[:n]
+        mask = valid[lo:n]
         if not mask.any():
             continue
-        kv = keys[:n][mask]
-        vv = vals[:n][mask]
+        kv = keys[lo:n][mask]
+        vv = vals[lo:n][mask]
         s = float(scale) * (q[i] @ kv.T)              # [G, n_visible]
         m = s.max(axis=1, keepdims=True)
         p = np.exp(s - m)
@@ -182,7 +201,7 @@ def attend_rows(q, keys, vals, valid, scale, q_len):
 
 
 def paged_attention(query, key_cache, value_cache, block_tables, context_lens,
-                    scale, gqa_factor, fmt, q_fmt=None, block_size=BLOCK_SIZE):
+                    scale, gqa_factor, fmt, q_fmt=None, block_size=BLOCK_SIZE, window=0):
     """Paged-attention decode, evaluated as the plain definition.
 
     query: uint16 bits ``[B, Q, Hq, D]``; caches: uint16 bits
@@ -192,7 +211,8 @@ def paged_attention(query, key_cache, value_cache, block_tables, context_lens,
     Query head ``h`` reads KV head ``h // gqa_factor`` ("The KV Cache",
     arithmetic paragraph: the stride trick ``kv_head_idx = tid.y /
     gqa_factor``).  The softmax scale is the float32 value the kernel receives,
-    widened to float64.
+    widened to float64.  ``window`` > 0 restricts each row to its most recent
+    positions (``window_start``).
     """
     q_fmt = q_fmt or fmt
     qv = decode(query, q_fmt)
@@ -201,11 +221,11 @@ def paged_attention(query, key_cache, value_cache, block_tables, context_lens,
         return decode(key_cache[blk, off], fmt), decode(value_cache[blk, off], fmt)
 
     return _attend(qv, rows, key_cache.shape[0], key_cache.shape[2], block_tables,
-                   context_lens, scale, gqa_factor, block_size)
+                   context_lens, scale, gqa_factor, block_size, window)
 
 
 def _attend(qv, read_rows, num_blocks, hkv, block_tables, context_lens, scale,
-            gqa_factor, block_size):
+            gqa_factor, block_size, window=0):
     """Shared driver: resolve each sequence, decode only its rows, attend."""
     b_count, q_len, hq, d = qv.shape
     if hq != hkv * gqa_factor:
@@ -220,7 +240,7 @@ def _attend(qv, read_rows, num_blocks, hkv, block_tables, context_lens, scale,
         for g in range(hkv):
             heads = slice(g * gqa_factor, (g + 1) * gqa_factor)
             out[b, :, heads, :] = attend_rows(qv[b, :, heads, :], keys[:, g, :], vals[:, g, :],
-                                              valid, scale64, q_len)
+                                              valid, scale64, q_len, window)
     return out
 
 

@@ -66,6 +66,8 @@ SIGNATURES = {
                                               + [_i, _i, _p, _sz, _p], _i),
     "paged_attention_decode_splitkv_append_partials": ([_p, _p, _p] + _ATTN[3:]
                                                        + [_i, _i, _p, _sz, _p], _i),
+    "paged_attention_decode_window": (_ATTN + [_i, _p], _i),
+    "paged_attention_decode_splitkv_window": (_ATTN + [_i, _i, _i, _p, _sz, _p], _i),
 }
 for _name, (_args, _res) in SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -276,6 +278,39 @@ def paged_attention_decode_splitkv_append_partials(query, new_key, new_value, ke
     _check(lib.paged_attention_decode_splitkv_append_partials(
         *args[2:], float(scale), int(max_context_len), int(partition_size), _ptr(workspace),
         nbytes, _stream(dev)))
+
+
+def paged_attention_decode_window(out, query, key_cache, value_cache, block_tables, context_lens,
+                                  scale, gqa_factor, sliding_window):
+    """Direct decode over each row's ``sliding_window`` most recent positions."""
+    dev = _dev(out, query, key_cache, value_cache, block_tables, context_lens)
+    B, Q, Hq, D = _attn_common(out, query, block_tables, context_lens, gqa_factor)
+    _expect(key_cache.shape == value_cache.shape and key_cache.shape[2:] == (Hq // gqa_factor, D),
+            "caches must be [NB, 16, Hq/G, D]")
+    _expect(query.dtype == key_cache.dtype == value_cache.dtype, "query/cache dtype mismatch")
+    _check(lib.paged_attention_decode_window(
+        _ptr(out), _dtype_code(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+        _dtype_code(key_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        B, Q, Hq, gqa_factor, D, key_cache.shape[1], key_cache.shape[0], float(scale),
+        int(sliding_window), _stream(dev)))
+
+
+def paged_attention_decode_splitkv_window(out, query, key_cache, value_cache, block_tables,
+                                          context_lens, scale, gqa_factor, sliding_window,
+                                          max_context_len, partition_size, workspace):
+    """Split-KV decode over each row's ``sliding_window`` most recent positions."""
+    dev = _dev(out, query, key_cache, value_cache, block_tables, context_lens, workspace)
+    B, Q, Hq, D = _attn_common(out, query, block_tables, context_lens, gqa_factor)
+    _expect(key_cache.shape == value_cache.shape and key_cache.shape[2:] == (Hq // gqa_factor, D),
+            "caches must be [NB, 16, Hq/G, D]")
+    _expect(query.dtype == key_cache.dtype == value_cache.dtype, "query/cache dtype mismatch")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.paged_attention_decode_splitkv_window(
+        _ptr(out), _dtype_code(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+        _dtype_code(key_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        B, Q, Hq, gqa_factor, D, key_cache.shape[1], key_cache.shape[0], float(scale),
+        int(sliding_window), int(max_context_len), int(partition_size), _ptr(workspace), nbytes,
+        _stream(dev)))
 
 
 def _k8v4_check(query, gqa_factor, k_cache, k_scale, v_cache, v_scale, v_zero):

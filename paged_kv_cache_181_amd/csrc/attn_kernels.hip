@@ -28,9 +28,11 @@
 //     transposed as the A operand.  Output lane l holds row l % 16's dims
 //     16n + 4*(l/16) + r, so the softmax rescale is one factor per lane.
 //   - Loads of the next block are issued before the current block is used.
-//   - Positions past the length, past a row's causal limit, or in a block whose
-//     table entry is out of range are excluded by selecting -inf scores, and V
-//     rows past the length are zeroed, so NaN garbage there never propagates.
+//   - Positions past the length, past a row's causal limit, before a row's
+//     sliding window, or in a block whose table entry is out of range are
+//     excluded by selecting -inf scores, and V rows that no row may see are
+//     zeroed, so NaN garbage there never propagates.  Blocks wholly before
+//     every row's window are not read.
 //
 // K8/V4 storage: int8 K codes are converted exactly to the MFMA element type and
 // the per-token scale multiplies the scores; 4-bit V codes are converted exactly
@@ -257,11 +259,11 @@ void attn_partition_kernel(const AttnArgs a) {
   // the sequence's table row; entries past max_blocks read as 0 (never used)
   const auto btr = span_rsrc(a.block_tables + (int64_t)b * a.max_blocks,
                              (uint32_t)a.max_blocks * 4u);
-  const int bb = p * a.part_blocks;
+  const int bb_guess = p * a.part_blocks;       // the partition's first block without a window
   int per = (a.part_blocks + NW - 1) / NW;
   int tbl_next;
   {
-    const int e = bb + w * per + lane;
+    const int e = bb_guess + w * per + lane;
     tbl_next = lane < per ? buf_load<int>(btr, (uint32_t)e * 4u) : 0;
   }
   constexpr int QCW = RT * (D / 8);                         // 16-byte query chunks per wave
@@ -285,8 +287,18 @@ void attn_partition_kernel(const AttnArgs a) {
   const bool append = KV != Fmt::K8V4 && a.new_k != nullptr;
   const int Lc = append ? max(L - Q, 0) : L;                // positions read from the cache
   const int nblk = (Lc + kBlock - 1) / kBlock;
-  const int p_new = append && L > 0 ? min((L - 1) / kBlock / a.part_blocks, a.num_parts - 1) : -1;
-  if (split && bb >= nblk && p != p_new) {                  // partition past this sequence:
+  // Sliding window W: row i (position L-Q+i) sees positions L-Q+i-W+1 ..
+  // L-Q+i, so nothing before lo0 (row 0's first position) is read at all,
+  // and partitions are counted from lo0's block (the grid covers the window).
+  const int W = a.window;
+  const int lo0 = W > 0 ? max(L - Q - W + 1, 0) : 0;
+  const int sb = lo0 / kBlock;
+  const int bb = sb + bb_guess;                             // the partition's first block
+  const int p_new = append && L > 0
+                        ? min(((L - 1) / kBlock - sb) / a.part_blocks, a.num_parts - 1) : -1;
+  const int be = (p == a.num_parts - 1) ? nblk : min(nblk, bb + a.part_blocks);
+  const int b0 = bb;                                        // first block of the partition read
+  if (split && b0 >= be && p != p_new) {                    // partition with nothing to read:
     // mark it empty (max -inf, sum 0) so the merge can read every partition
     // without first reading the sequence length
     for (int rr = threadIdx.x; rr < GQ; rr += NW * kWave) {
@@ -296,13 +308,15 @@ void attn_partition_kernel(const AttnArgs a) {
     }
     return;
   }
-  const int be = (p == a.num_parts - 1) ? nblk : min(nblk, bb + a.part_blocks);
-  if (be - bb > a.part_blocks) {        // a last partition longer than the others
-    per = (be - bb + NW - 1) / NW;      // (length past the grid): runs resized
-    const int e = bb + w * per + lane;
+  if (b0 != bb_guess || be - bb > a.part_blocks) {
+    // partitions counted from a window's start, or a last partition longer
+    // than the others (length past the grid): the runs are spread evenly
+    // over the blocks actually read
+    per = (be - b0 + NW - 1) / NW;
+    const int e = b0 + w * per + lane;
     tbl_next = lane < per ? buf_load<int>(btr, (uint32_t)e * 4u) : 0;
   }
-  const int w0 = bb + w * per;                              // first block of this wave's run
+  const int w0 = b0 + w * per;                              // first block of this wave's run
   const int nmine = max(0, min(per, be - w0));
 
   // the query row this lane owns: rho = iq * G + hl (lanes past G*q_len
@@ -311,6 +325,8 @@ void attn_partition_kernel(const AttnArgs a) {
   const int iq = row_ok ? rho / G : 0;
   const int nvis = row_ok ? (L - Q + iq + 1) : L;           // visible positions of the row
   const int full_lim = L - Q + 1;                           // every row sees j < full_lim
+  const int lo_row = W > 0 && row_ok ? max(L - Q + iq - W + 1, 0) : lo0;   // window start
+  const int lo_max = W > 0 ? max(L - W, 0) : 0;             // every row sees j >= lo_max
 
   // append form: the table entry of each new token's position (lane rho = token)
   int tnew = -1;
@@ -332,8 +348,11 @@ void attn_partition_kernel(const AttnArgs a) {
     const int pb = __builtin_amdgcn_readlane(tblv, j & 63);
     const bool ok = j < cnt && pb >= 0 && (int64_t)pb < a.num_blocks;
     load_block<KV, D>(a, ok ? pb : 0, ok, loff, br);
-    const int left = Lc - (w0 + c0 + j) * kBlock;           // cache tokens from this block on
-    return !ok ? 0u : left >= kBlock ? 0xffffu : (1u << max(left, 0)) - 1u;
+    const int jb = (w0 + c0 + j) * kBlock;                  // the block's first position
+    const int left = Lc - jb;                               // cache tokens from it on
+    uint32_t m = left >= kBlock ? 0xffffu : (1u << max(left, 0)) - 1u;
+    if (lo0 > jb) m &= ~((1u << min(lo0 - jb, kBlock)) - 1u);   // before every window
+    return ok ? m : 0u;
   };
   BlockRegs<KV, D> r0, r1;
   uint32_t ok0 = fetch(0, 0, min(64, nmine), r0), ok1 = 0u;
@@ -368,7 +387,7 @@ void attn_partition_kernel(const AttnArgs a) {
   // whether token t holds data (wave-uniform).
   auto process = [&](int j0, uint32_t vmask, BlockRegs<KV, D>& br) {
     const bool tail = vmask != 0xffffu;                      // some tokens hold no data
-    const bool full = !tail && j0 + kBlock <= full_lim;      // no masking needed at all
+    const bool full = !tail && j0 >= lo_max && j0 + kBlock <= full_lim;   // no masking at all
     const bool tok_ok = (vmask >> rho) & 1u;                 // this lane's token (rho) exists
 
     // ---- stage V in load-lane order: the 16-byte chunk (m, c) of token t at
@@ -455,7 +474,7 @@ void attn_partition_kernel(const AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = j0 + 4 * qd + r;
-        if (!((vmask >> (4 * qd + r)) & 1u) || j >= nvis) sv[r] = kNegInf;
+        if (!((vmask >> (4 * qd + r)) & 1u) || j >= nvis || j < lo_row) sv[r] = kNegInf;
       }
     }
     const float mx = quarter_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));

@@ -38,6 +38,7 @@ struct AttnArgs {
   float* ws_l;                   // split form: [B*Q*Hq, P] softmax denominators
   const void* new_k;             // append form (16-bit only): [B*Q, Hkv, D] new rows, else NULL
   const void* new_v;             // append form: [B*Q, Hkv, D]
+  int window;                    // sliding window in positions (0: the whole context)
 };
 
 // kv_fmt: 0 f16, 1 bf16, 3 k8v4; q_fmt: 0 f16, 1 bf16 (must equal kv_fmt unless k8v4).

@@ -554,3 +554,85 @@ def test_append_partials_then_merge_equals_the_single_call(P):
     torch.cuda.synchronize()
     assert torch.equal(out_a, out_b)
     assert torch.equal(k, k_a) and torch.equal(v, v_a)
+
+
+# ------------------------------------------------------------------ sliding window
+
+WINDOW_CASES = [
+    ("small_f16_d64", 1), ("small_f16_d64", 15), ("small_f16_d64", 16), ("small_f16_d64", 17),
+    ("small_f16_d64", 100), ("small_bf16_d128_g4", 33), ("small_verify_q4", 1),
+    ("small_verify_q4", 5), ("small_verify_q4", 40), ("small_g8_q2", 7), ("edge_lengths", 2),
+    ("edge_lengths", 16), ("long32k", 2048), ("long32k", 4000),
+]
+_window_refs = {}
+
+
+def window_ref(name, window):
+    key = (name, window)
+    if key not in _window_refs:
+        case, _ = get_case(name)
+        _window_refs[key] = oracle.paged_attention(
+            case.query, case.key_cache, case.value_cache, case.block_tables, case.context_lens,
+            case.scale, case.gqa_factor, case.fmt, window=window)
+    return _window_refs[key]
+
+
+def run_window(P, dc, window, *, split, psize=512, out_dtype=torch.float32, k=None, v=None):
+    c = dc.case
+    k = dc.k if k is None else k
+    v = dc.v if v is None else v
+    out = torch.full(dc.q.shape, float("nan"), dtype=out_dtype, device="cuda")
+    if split:
+        mcl = int(dc.cl.max().item())
+        B, Q, Hq, D = dc.q.shape
+        span = min(mcl, window + Q + 15) if window > 0 else mcl    # the documented grid span
+        n = P.splitkv_workspace_size(B, Q, Hq, D, span, psize)
+        ws = torch.full((max(n, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        P.paged_attention_decode_splitkv_window(out, dc.q, k, v, dc.bt, dc.cl, c.scale,
+                                                c.gqa_factor, window, mcl, psize, ws)
+    else:
+        P.paged_attention_decode_window(out, dc.q, k, v, dc.bt, dc.cl, c.scale, c.gqa_factor,
+                                        window)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("name,window", WINDOW_CASES)
+@pytest.mark.parametrize("split,psize", [(False, 0), (True, 512), (True, 32)])
+def test_window_matches_oracle(P, name, window, split, psize):
+    case, _ = get_case(name)
+    if case.name == "long32k" and not split:
+        pytest.skip("the 32K single sequence is a split-KV workload")
+    ref = window_ref(name, window)
+    dc = DevCase(case)
+    out = run_window(P, dc, window, split=split, psize=psize or 512)
+    err = max_err(out, ref)
+    assert err <= 2e-4, f"{name} W={window}: fp32-out max abs err {err}"
+
+
+def test_window_zero_is_the_plain_decode(P):
+    case, _ = get_case("small_verify_q4")
+    dc = DevCase(case)
+    for split in (False, True):
+        a = run_window(P, dc, 0, split=split, psize=32)
+        b = run_decode(P, dc, split=split, partition_size=32)
+        assert torch.equal(a, b)
+
+
+def test_window_never_uses_positions_outside_every_window(P):
+    """Positions before every row's window hold NaN: the result is unchanged."""
+    case, _ = get_case("small_verify_q4")
+    window = 9
+    dc = DevCase(case)
+    clean = [run_window(P, dc, window, split=s, psize=32) for s in (False, True)]
+    kc, vc = case.key_cache.copy(), case.value_cache.copy()
+    for b in range(case.batch):
+        L = int(case.context_lens[b])
+        lo0 = max(L - case.q_len - window + 1, 0)
+        for j in range(lo0):
+            blk, off = case.block_tables[b, j // 16], j % 16
+            kc[blk, off] = 0x7E00                  # fp16 NaN
+            vc[blk, off] = 0x7E00
+    k, v = bits_to_dev(kc, case.fmt), bits_to_dev(vc, case.fmt)
+    for s, ref in zip((False, True), clean):
+        assert torch.equal(run_window(P, dc, window, split=s, psize=32, k=k, v=v), ref)

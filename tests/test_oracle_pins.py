@@ -55,9 +55,10 @@ def decode_bits(bits, fmt):
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def sdpa_reference(case):
+def sdpa_reference(case, window=0):
     """torch.nn.functional.scaled_dot_product_attention (float64, CPU) with an
-    explicit bottom-right causal mask and KV heads expanded per the GQA rule."""
+    explicit bottom-right causal mask (a band of ``window`` positions when
+    ``window`` > 0) and KV heads expanded per the GQA rule."""
     out = np.zeros(case.query.shape, dtype=np.float64)
     G = case.gqa_factor
     for b in range(case.batch):
@@ -71,6 +72,8 @@ def sdpa_reference(case):
         rows = torch.arange(Q)[:, None]
         cols = torch.arange(L)[None, :]
         mask = cols <= (L - Q + rows)
+        if window > 0:
+            mask = mask & (cols > (L - Q + rows) - window)
         o = torch.nn.functional.scaled_dot_product_attention(
             q[None], k[None], v[None], attn_mask=mask, scale=float(np.float32(case.scale)))
         out[b] = o[0].permute(1, 0, 2).numpy()
@@ -564,6 +567,45 @@ def test_generators_structure():
 # 6. planted mistakes: each plausible slip in the oracle fails a pin above
 # ---------------------------------------------------------------------------
 
+# ---------------------------------------------------------------------------
+# sliding window
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("q_len", [1, 4])
+@pytest.mark.parametrize("window", [1, 3, 16, 17, 40])
+def test_window_matches_banded_sdpa(q_len, window):
+    case = small_case(60 + q_len, q_len=q_len, batch=4, lengths=[5, 33, 64, 90])
+    got = run_oracle(case, window=window)
+    assert np.abs(got - sdpa_reference(case, window=window)).max() < 1e-12
+
+
+def test_window_of_the_whole_context_is_no_window():
+    case = small_case(62, q_len=4, batch=3, lengths=[4, 40, 77])
+    plain = run_oracle(case)
+    assert np.array_equal(run_oracle(case, window=77), plain)
+    assert np.array_equal(run_oracle(case, window=10_000), plain)
+
+
+def test_window_one_returns_the_row_s_own_value():
+    case = small_case(63, q_len=3, batch=2, lengths=[20, 45])
+    out = run_oracle(case, window=1)
+    G = case.gqa_factor
+    for b in range(case.batch):
+        L = int(case.context_lens[b])
+        V = contiguous_kv(case.value_cache, case.block_tables[b], L, case.fmt)
+        for i in range(case.q_len):
+            for h in range(case.num_q_heads):
+                assert np.array_equal(out[b, i, h], V[L - case.q_len + i, h // G])
+
+
+def test_planted_window_off_by_one_is_caught(monkeypatch):
+    case = small_case(64, q_len=2, batch=3, lengths=[30, 50, 70])
+    monkeypatch.setattr(P, "window_start",
+                        lambda length, q_len, i, window: max(length - q_len + i - window, 0)
+                        if window > 0 else 0)
+    assert np.abs(run_oracle(case, window=8) - sdpa_reference(case, window=8)).max() > 1e-3
+
+
 def _sdpa_error(case):
     return np.abs(run_oracle(case) - sdpa_reference(case)).max()
 
@@ -578,10 +620,10 @@ def test_planted_gqa_modulo_mapping_is_caught(monkeypatch):
     case = small_case(42, hq=8, hkv=2)
     orig = P._attend
 
-    def wrong(qv, read_rows, nb, hkv, bt, cl, scale, G, bs):
+    def wrong(qv, read_rows, nb, hkv, bt, cl, scale, G, bs, window=0):
         # route query head h to KV head h % hkv instead of h // G
         perm = np.concatenate([np.arange(g, qv.shape[2], hkv) for g in range(hkv)])
-        out = orig(qv[:, :, perm], read_rows, nb, hkv, bt, cl, scale, G, bs)
+        out = orig(qv[:, :, perm], read_rows, nb, hkv, bt, cl, scale, G, bs, window)
         res = np.empty_like(out)
         res[:, :, perm] = out
         return res
