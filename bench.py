@@ -334,6 +334,41 @@ def other_workload(name, P, W, torch, steps, warmup):
             "writes_per_layer": T, "kv_format": "k8v4" if name == "k8v4" else fmt}
 
 
+def gather_workload(P, W, torch, steps, warmup, layers=8):
+    """gather_kv_cache of every sequence of the Llama-3-8B-shaped batch
+    (bf16, 32 sequences of 512..4096 tokens) into packed rows, per layer."""
+    import numpy as np
+    lay, B, Q, Hq, Hkv, D, fmt = W.layout_of("llama8b_batch", 2)
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2 * 1000 + 11)
+    NB = lay.num_blocks
+    lens = lay.context_lens.astype(np.int64)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(dev)
+    total = int(lens.sum())
+    bt = torch.from_numpy(lay.block_tables).to(dev)
+    K = [torch.randn(NB, 16, Hkv, D, generator=gen, device=dev, dtype=torch.bfloat16)
+         for _ in range(layers)]
+    V = [torch.randn(NB, 16, Hkv, D, generator=gen, device=dev, dtype=torch.bfloat16)
+         for _ in range(layers)]
+    ko = [torch.empty(total, Hkv, D, device=dev, dtype=torch.bfloat16) for _ in range(layers)]
+    vo = [torch.empty_like(x) for x in ko]
+    mx = int(lens.max())
+
+    def step():
+        for l in range(layers):
+            P.gather_kv_cache(K[l], V[l], bt, cu, mx, ko[l], vo[l])
+    ms = time_steps(torch, graph_of(torch, step).replay, steps, warmup)
+    us = ms * 1e3 / layers
+    read = total * Hkv * D * 2 * 2
+    return {"us_per_layer": round(us, 3), "kv_bytes_read_per_layer": read,
+            "kv_stream_gbs": round(read / (us * 1e-6) / 1e9, 2),
+            "hbm_gbs_read_plus_write": round(2 * read / (us * 1e-6) / 1e9, 2),
+            "pct_of_hbm_peak": round(100 * 2 * read / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+            "layers": layers, "form": "gather_kv_cache of all 32 sequences (K and V), HIP graph",
+            "kv_format": "bf16"}
+
+
 def copy_calibration(torch):
     """A plain device copy of known size: 1 GiB read + 1 GiB written per launch.
     rocprofv3's FETCH_SIZE / WRITE_SIZE for these launches give the scale
@@ -426,6 +461,10 @@ def main():
             result["other_workloads"][name] = other_workload(name, P, W, torch, args.steps,
                                                              args.warmup)
             torch.cuda.empty_cache()
+        log("timing gather_kv_cache")
+        result["other_workloads"]["gather_llama8b_batch"] = gather_workload(P, W, torch,
+                                                                            args.steps, args.warmup)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

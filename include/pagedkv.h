@@ -100,6 +100,32 @@ int kv_cache_write(const void* key, const void* value, void* key_cache, void* va
                    int head_dim, int block_size, int64_t num_blocks, int dtype, void* stream);
 
 /*
+ * gather_kv_cache — the inverse of the slot scatter: every sequence's cached
+ * rows copied out of the pages into packed contiguous arrays for dense
+ * consumers ("The KV Cache" (metalworking), layout paragraph: the
+ * gather_kv_cache kernel of the paged kernel family).
+ *   key_cache, value_cache: [num_blocks, block_size, num_kv_heads, head_dim]
+ *   block_tables:  int32 [batch, max_blocks_per_seq]
+ *   cu_seq_lens:   int32 [batch + 1], device; sequence b fills output rows
+ *                  cu_seq_lens[b] .. cu_seq_lens[b+1] - 1 with its positions
+ *                  0 .. L_b - 1, L_b = cu_seq_lens[b+1] - cu_seq_lens[b]
+ *                  (clamped to max_blocks_per_seq * 16 like every length)
+ *   max_seq_len:   host bound on every L_b (sizes the grid; positions past
+ *                  it are not copied)
+ *   key_out, value_out: [total_tokens, num_kv_heads, head_dim], written only
+ *                  in the rows the sequences cover (rows outside
+ *                  [0, total_tokens) are never written)
+ * Position j comes from block block_tables[b][j / 16], row j % 16; if that
+ * entry is outside [0, num_blocks) the output row is zero.  A plain copy
+ * (bit-exact); dtype (PKV_F16 or PKV_BF16) only fixes the element size.
+ */
+int gather_kv_cache(const void* key_cache, const void* value_cache, int dtype,
+                    const int32_t* block_tables, int max_blocks_per_seq,
+                    const int32_t* cu_seq_lens, int batch, int max_seq_len, void* key_out,
+                    void* value_out, int64_t total_tokens, int num_kv_heads, int head_dim,
+                    int block_size, int64_t num_blocks, void* stream);
+
+/*
  * paged_attention_decode — one workgroup per (sequence, KV head), no workspace.
  *   out:          [batch, q_len, num_q_heads, head_dim] of out_dtype (f16, bf16 or f32)
  *   query:        [batch, q_len, num_q_heads, head_dim] of kv_dtype

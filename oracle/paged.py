@@ -245,6 +245,45 @@ def _attend(qv, read_rows, num_blocks, hkv, block_tables, context_lens, scale,
 
 
 # ---------------------------------------------------------------------------
+# gather_kv_cache: paged -> contiguous (the inverse of the slot scatter)
+# ---------------------------------------------------------------------------
+
+def gather_kv_cache(key_cache, value_cache, block_tables, cu_seq_lens, total_tokens,
+                    block_size=BLOCK_SIZE):
+    """Copy every sequence's cached rows out of the pages into packed arrays.
+
+    "The KV Cache" (metalworking), layout paragraph, names a gather_kv_cache
+    kernel beside reshape_and_cache; reading (its arguments are not given):
+    it is the inverse of the slot scatter, laying each sequence's positions
+    ``0 .. L_b - 1`` out contiguously for dense consumers.  Sequence ``b``
+    fills output rows ``cu_seq_lens[b] .. cu_seq_lens[b+1] - 1`` (so
+    ``L_b = cu_seq_lens[b+1] - cu_seq_lens[b]``); position ``j`` comes from
+    block ``block_tables[b][j // block_size]``, row ``j % block_size``.
+    Readings: a length is clamped to ``[0, max_blocks * block_size]`` like
+    every length; a position whose table entry names no pool block gives a
+    zero row; output rows outside ``[0, total_tokens)`` are not written; rows
+    no sequence covers stay zero.  Returns ``(keys, values)``, each
+    ``[total_tokens, Hkv, D]`` of the caches' element type.
+    """
+    bt = np.asarray(block_tables)
+    cu = np.asarray(cu_seq_lens, dtype=np.int64)
+    nb = key_cache.shape[0]
+    out_k = np.zeros((total_tokens,) + key_cache.shape[2:], dtype=key_cache.dtype)
+    out_v = np.zeros((total_tokens,) + value_cache.shape[2:], dtype=value_cache.dtype)
+    for b in range(len(cu) - 1):
+        length = effective_length(int(cu[b + 1] - cu[b]), bt.shape[1], block_size)
+        for j in range(length):
+            row = int(cu[b]) + j
+            if not 0 <= row < total_tokens:
+                continue
+            blk = int(bt[b, j // block_size])
+            if 0 <= blk < nb:
+                out_k[row] = key_cache[blk, j % block_size]
+                out_v[row] = value_cache[blk, j % block_size]
+    return out_k, out_v
+
+
+# ---------------------------------------------------------------------------
 # The decode step as one call: write the new rows where the tables put them,
 # then attend
 # ---------------------------------------------------------------------------

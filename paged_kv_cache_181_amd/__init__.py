@@ -19,7 +19,7 @@ _EXPORTS = (
     "paged_attention_decode_splitkv_partials", "paged_attention_decode_splitkv_k8v4_partials",
     "paged_attention_decode_splitkv_merge", "paged_attention_decode_append",
     "paged_attention_decode_splitkv_append", "paged_attention_decode_splitkv_append_partials",
-    "paged_attention_decode_window", "paged_attention_decode_splitkv_window",
+    "paged_attention_decode_window", "paged_attention_decode_splitkv_window", "gather_kv_cache",
 )
 
 __all__ = list(_EXPORTS)

@@ -67,6 +67,7 @@ SIGNATURES = {
     "paged_attention_decode_splitkv_append_partials": ([_p, _p, _p] + _ATTN[3:]
                                                        + [_i, _i, _p, _sz, _p], _i),
     "paged_attention_decode_window": (_ATTN + [_i, _p], _i),
+    "gather_kv_cache": ([_p, _p, _i, _p, _i, _p, _i, _i, _p, _p, _i64, _i, _i, _i, _i64, _p], _i),
     "paged_attention_decode_splitkv_window": (_ATTN + [_i, _i, _i, _p, _sz, _p], _i),
 }
 for _name, (_args, _res) in SIGNATURES.items():
@@ -311,6 +312,29 @@ def paged_attention_decode_splitkv_window(out, query, key_cache, value_cache, bl
         B, Q, Hq, gqa_factor, D, key_cache.shape[1], key_cache.shape[0], float(scale),
         int(sliding_window), int(max_context_len), int(partition_size), _ptr(workspace), nbytes,
         _stream(dev)))
+
+
+def gather_kv_cache(key_cache, value_cache, block_tables, cu_seq_lens, max_seq_len, key_out,
+                    value_out):
+    """Copy each sequence's cached rows into packed [total_tokens, Hkv, D]
+    outputs: sequence b fills rows cu_seq_lens[b] .. cu_seq_lens[b+1] - 1."""
+    torch = _torch()
+    dev = _dev(key_cache, value_cache, block_tables, cu_seq_lens, key_out, value_out)
+    _expect(key_cache.dim() == 4 and key_cache.shape == value_cache.shape,
+            "caches must be [NB, 16, Hkv, D]")
+    _expect(block_tables.dtype == torch.int32 and block_tables.dim() == 2,
+            "block_tables must be int32 [B, max_blocks]")
+    _expect(cu_seq_lens.dtype == torch.int32 and cu_seq_lens.shape == (block_tables.shape[0] + 1,),
+            "cu_seq_lens must be int32 [B + 1]")
+    _expect(key_out.shape == value_out.shape and key_out.shape[1:] == key_cache.shape[2:],
+            "outputs must be [total_tokens, Hkv, D]")
+    _expect(key_out.dtype == value_out.dtype == key_cache.dtype == value_cache.dtype,
+            "output/cache dtype mismatch")
+    _check(lib.gather_kv_cache(
+        _ptr(key_cache), _ptr(value_cache), _dtype_code(key_cache), _ptr(block_tables),
+        block_tables.shape[1], _ptr(cu_seq_lens), block_tables.shape[0], int(max_seq_len),
+        _ptr(key_out), _ptr(value_out), key_out.shape[0], key_cache.shape[2], key_cache.shape[3],
+        key_cache.shape[1], key_cache.shape[0], _stream(dev)))
 
 
 def _k8v4_check(query, gqa_factor, k_cache, k_scale, v_cache, v_scale, v_zero):

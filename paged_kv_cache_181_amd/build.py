@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpagedkv.so")
-SOURCES = ["api.hip", "write_kernels.hip", "attn_kernels.hip"]
+SOURCES = ["api.hip", "write_kernels.hip", "attn_kernels.hip", "gather_kernels.hip"]
 ARCH = "gfx950"
 
 

@@ -189,6 +189,35 @@ int kv_cache_write(const void* key, const void* value, void* key_cache, void* va
                        "kv_cache_write");
 }
 
+int gather_kv_cache(const void* key_cache, const void* value_cache, int dtype,
+                    const int32_t* block_tables, int max_blocks_per_seq,
+                    const int32_t* cu_seq_lens, int batch, int max_seq_len, void* key_out,
+                    void* value_out, int64_t total_tokens, int num_kv_heads, int head_dim,
+                    int block_size, int64_t num_blocks, void* stream) {
+  int rc = check_cache_geometry(num_kv_heads, head_dim, block_size, num_blocks);
+  if (rc) return rc;
+  if (dtype != PKV_F16 && dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "dtype must be PKV_F16 or PKV_BF16");
+  if (batch < 0 || max_blocks_per_seq < 0 || max_seq_len < 0 || total_tokens < 0)
+    return fail(PKV_ERR_SHAPE, "batch, max_blocks_per_seq, max_seq_len and total_tokens must "
+                               "be non-negative");
+  if (batch > 65535) return fail(PKV_ERR_UNSUPPORTED, "batch too large");
+  if (max_blocks_per_seq > (1 << 26))
+    return fail(PKV_ERR_UNSUPPORTED, "max_blocks_per_seq above 2^26");
+  if (batch == 0 || total_tokens == 0 || max_seq_len == 0 || max_blocks_per_seq == 0)
+    return ok();
+  if (!key_cache || !value_cache || !block_tables || !cu_seq_lens || !key_out || !value_out)
+    return fail(PKV_ERR_NULL, "a required pointer is NULL");
+  if (!aligned16(key_cache) || !aligned16(value_cache) || !aligned16(key_out) ||
+      !aligned16(value_out))
+    return fail(PKV_ERR_ALIGN, "caches and outputs must be 16-byte aligned");
+  return launch_result(pkv::launch_gather(key_cache, value_cache, block_tables,
+                                          max_blocks_per_seq, cu_seq_lens, batch, max_seq_len,
+                                          total_tokens, num_kv_heads, head_dim, num_blocks,
+                                          key_out, value_out, (hipStream_t)stream),
+                       "gather_kv_cache");
+}
+
 int kv_cache_write_k8v4(const void* key, const void* value, int in_dtype, int8_t* k_cache,
                         void* k_scale, uint8_t* v_cache, void* v_scale, void* v_zero,
                         const int64_t* slot_mapping, int64_t num_tokens, int num_kv_heads,

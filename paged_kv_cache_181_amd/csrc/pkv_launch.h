@@ -15,6 +15,14 @@ hipError_t launch_kv_write_k8v4(const void* key, const void* value, int in_dtype
                                 const int64_t* slots, int64_t num_tokens, int num_kv_heads,
                                 int head_dim, int64_t num_blocks, hipStream_t stream);
 
+// Packed copy of each sequence's cached rows (gather_kv_cache).  Only sequences
+// with cu_seq_lens[b+1] - cu_seq_lens[b] <= max_seq_len are copied in full.
+hipError_t launch_gather(const void* key_cache, const void* value_cache,
+                         const int32_t* block_tables, int max_blocks, const int32_t* cu_seq_lens,
+                         int batch, int max_seq_len, int64_t total_tokens, int num_kv_heads,
+                         int head_dim, int64_t num_blocks, void* key_out, void* value_out,
+                         hipStream_t stream);
+
 // Everything the attention kernels need; filled by the ABI layer after validation.
 struct AttnArgs {
   void* out;

@@ -186,3 +186,29 @@ def test_append_argument_errors(P):
     for i in (0, 2, 3, 4, 5, 6, 8, 10):
         zero[i] = None
     assert lib.paged_attention_decode_append(*zero, None) == 0
+
+
+def test_gather_argument_errors(P):
+    lib = P.lib
+    # key_cache, value_cache, dtype, bt, mb, cu, B, max_len, k_out, v_out, total, Hkv, D, bs, nb
+    base = [FAKE, FAKE, 0, FAKE, 4, FAKE, 2, 64, FAKE, FAKE, 100, 8, 128, 16, 64]
+    bad = list(base)
+    bad[2] = 2
+    assert lib.gather_kv_cache(*bad, None) == -3
+    bad = list(base)
+    bad[5] = None
+    assert lib.gather_kv_cache(*bad, None) == -1
+    bad = list(base)
+    bad[8] = ctypes.c_void_p(4100)
+    assert lib.gather_kv_cache(*bad, None) == -6
+    bad = list(base)
+    bad[12] = 96
+    assert lib.gather_kv_cache(*bad, None) == -3
+    bad = list(base)
+    bad[10] = -1
+    assert lib.gather_kv_cache(*bad, None) == -2
+    empty = list(base)
+    empty[10] = 0
+    for i in (0, 1, 3, 5, 8, 9):
+        empty[i] = None
+    assert lib.gather_kv_cache(*empty, None) == 0

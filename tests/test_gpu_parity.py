@@ -636,3 +636,71 @@ def test_window_never_uses_positions_outside_every_window(P):
     k, v = bits_to_dev(kc, case.fmt), bits_to_dev(vc, case.fmt)
     for s, ref in zip((False, True), clean):
         assert torch.equal(run_window(P, dc, window, split=s, psize=32, k=k, v=v), ref)
+
+
+# ------------------------------------------------------------------ gather_kv_cache
+
+def run_gather(P, case, bt=None, cl=None, total=None, max_len=None, fill=0x5A5A):
+    """cu_seq_lens from the lengths; outputs pre-filled with a sentinel."""
+    lens = (case.context_lens if cl is None else cl).astype(np.int64)
+    cu = np.concatenate([[0], np.cumsum(np.maximum(lens, 0))]).astype(np.int32)
+    total = int(cu[-1]) if total is None else total
+    k, v = bits_to_dev(case.key_cache, case.fmt), bits_to_dev(case.value_cache, case.fmt)
+    hkv, d = case.num_kv_heads, case.head_dim
+    ko = torch.full((total, hkv, d), fill, dtype=torch.int16, device="cuda").view(k.dtype)
+    vo = torch.full((total, hkv, d), fill, dtype=torch.int16, device="cuda").view(k.dtype)
+    btd = torch.from_numpy(case.block_tables if bt is None else bt).cuda()
+    P.gather_kv_cache(k, v, btd, torch.from_numpy(cu).cuda(),
+                      int(max(lens.max(), 0)) if max_len is None else max_len, ko, vo)
+    torch.cuda.synchronize()
+    return dev_to_bits(ko), dev_to_bits(vo), cu, total
+
+
+@pytest.mark.parametrize("name", ["tiny", "small_f16_d64", "small_bf16_d128_g4", "small_g1",
+                                  "edge_lengths", "llama8b_batch", "long32k"])
+def test_gather_bit_exact(P, name):
+    case, _ = get_case(name)
+    gk, gv, cu, total = run_gather(P, case)
+    rk, rv = oracle.gather_kv_cache(case.key_cache, case.value_cache, case.block_tables, cu, total)
+    assert np.array_equal(gk, rk) and np.array_equal(gv, rv)
+
+
+def test_gather_edge_rules(P):
+    """Out-of-pool table entries give zero rows; rows past total_tokens are
+    never written; a length past the table is clamped."""
+    case = small(130, batch=3, num_q_heads=8, num_kv_heads=2, head_dim=64, lengths=[40, 33, 20])
+    bt = case.block_tables.copy()
+    bt[0, 1] = case.num_blocks + 5
+    bt[1, 0] = -1
+    cl = case.context_lens.copy()
+    cl[2] = 10_000                                     # clamped to the table's blocks
+    mb = bt.shape[1]
+    lens = np.minimum(cl.astype(np.int64), mb * 16)
+    cu = np.concatenate([[0], np.cumsum(np.asarray(cl, np.int64))]).astype(np.int32)
+    total = int(lens[0] + lens[1] + 7)                 # cuts into sequence 2
+    k, v = bits_to_dev(case.key_cache, case.fmt), bits_to_dev(case.value_cache, case.fmt)
+    ko = torch.full((total, 2, 64), 0x5A5A, dtype=torch.int16, device="cuda").view(k.dtype)
+    vo = torch.full((total, 2, 64), 0x5A5A, dtype=torch.int16, device="cuda").view(k.dtype)
+    P.gather_kv_cache(k, v, torch.from_numpy(bt).cuda(), torch.from_numpy(cu).cuda(), mb * 16,
+                      ko, vo)
+    torch.cuda.synchronize()
+    rk, rv = oracle.gather_kv_cache(case.key_cache, case.value_cache, bt, cu, total)
+    assert np.array_equal(dev_to_bits(ko), rk) and np.array_equal(dev_to_bits(vo), rv)
+
+
+def test_gather_then_write_round_trip(P):
+    """Rows gathered out of the cache and scattered back to the same slots
+    leave the cache unchanged."""
+    case, _ = get_case("small_bf16_d128_g4")
+    gk, gv, cu, total = run_gather(P, case)
+    slots = np.concatenate([[W.slot_of(case.block_tables, b, j)
+                             for j in range(int(case.context_lens[b]))]
+                            for b in range(case.batch)]).astype(np.int64)
+    k = torch.zeros_like(bits_to_dev(case.key_cache, case.fmt))
+    v = torch.zeros_like(k)
+    P.kv_cache_write(bits_to_dev(gk, case.fmt), bits_to_dev(gv, case.fmt), k, v,
+                     torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    used = np.unique(slots)
+    kb = dev_to_bits(k).reshape(-1, *case.key_cache.shape[2:])
+    assert np.array_equal(kb[used], case.key_cache.reshape(-1, *case.key_cache.shape[2:])[used])

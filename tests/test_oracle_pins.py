@@ -373,6 +373,35 @@ def test_decode_append_is_write_then_attend():
     assert np.abs(out - sdpa_reference(written)).max() < 1e-12
 
 
+def test_gather_inverts_the_slot_scatter():
+    # distinct rows scattered to the slots the tables give positions 0..L-1,
+    # then gathered back: the same rows, in position order
+    case = small_case(70, batch=3, lengths=[1, 17, 40])
+    lens = case.context_lens.astype(np.int64)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    total = int(cu[-1])
+    hkv, d = case.num_kv_heads, case.head_dim
+    rows_k = (np.arange(total * hkv * d, dtype=np.uint32) % 60000).astype(np.uint16).reshape(total, hkv, d)
+    rows_v = rows_k[::-1].copy()
+    slots = np.concatenate([[W.slot_of(case.block_tables, b, j) for j in range(int(lens[b]))]
+                            for b in range(case.batch)]).astype(np.int64)
+    kc, vc = oracle.kv_cache_write(rows_k, rows_v, np.zeros_like(case.key_cache),
+                                   np.zeros_like(case.value_cache), slots)
+    gk, gv = oracle.gather_kv_cache(kc, vc, case.block_tables, cu, total)
+    assert np.array_equal(gk, rows_k) and np.array_equal(gv, rows_v)
+
+
+def test_gather_by_hand_with_identity_table_and_edge_rules():
+    nb, hkv, d = 4, 1, 2
+    kc = np.arange(nb * 16 * hkv * d, dtype=np.uint16).reshape(nb, 16, hkv, d)
+    table = np.array([[0, 1, 2], [3, 9, -1]], np.int32)        # row 1: entry 1 names no block
+    cu = np.array([0, 20, 40])                                  # lengths 20 and 20
+    gk, _ = oracle.gather_kv_cache(kc, kc, table, cu, 38)       # last two rows out of range
+    assert np.array_equal(gk[:20], kc.reshape(nb * 16, hkv, d)[:20])     # identity table
+    assert np.array_equal(gk[20:36], kc[3])                     # block 3, positions 0..15
+    assert not gk[36:38].any()                                  # positions 16.. have no block
+
+
 def test_cache_size_closed_form_matches_page():
     g = golden("kv_cache_arithmetic.json")
     per_tok = oracle.kv_cache_bytes_per_token(g["num_layers"], g["num_kv_heads"], g["head_dim"], "f16")
