@@ -369,6 +369,56 @@ def gather_workload(P, W, torch, steps, warmup, layers=8):
             "kv_format": "bf16"}
 
 
+def cascade_workload(P, W, torch, steps, warmup, layers=8):
+    """Shared system prompt: 8 groups of 4 sequences share a 4096-token
+    prefix, each with its own 64..1024-token suffix (bf16, 32/8 heads, D 128).
+    Cascade (prefix read once per group) against plain split-KV (read once
+    per sequence); both partition 512."""
+    import numpy as np
+    lens, tables, NB, _, members, pre = W.shared_prefix_layout(W.rng_for(6), 8, 4, 4096, 64, 1024)
+    B, Q, Hq, Hkv, D, part = 32, 1, 32, 8, 128, 512
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(6 * 1000 + 13)
+    rnd = lambda *sh: torch.randn(sh, generator=gen, device=dev, dtype=torch.bfloat16)  # noqa: E731
+    K = [rnd(NB, 16, Hkv, D) for _ in range(layers)]
+    V = [rnd(NB, 16, Hkv, D) for _ in range(layers)]
+    q = [rnd(B, Q, Hq, D) for _ in range(layers)]
+    out = [torch.empty(B, Q, Hq, D, device=dev, dtype=torch.bfloat16) for _ in range(layers)]
+    bt = torch.from_numpy(tables).to(dev)
+    cl = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    mem = torch.from_numpy(members).to(dev)
+    pb = torch.from_numpy(pre).to(dev)
+    mcl, mpl = int(lens.max()), 4096
+    ws_c = torch.zeros(P.cascade_workspace_size(B, Q, Hq, D, mcl, mpl, part) // 4, device=dev)
+    ws_p = torch.zeros(P.splitkv_workspace_size(B, Q, Hq, D, mcl, part) // 4, device=dev)
+    scale = float(1.0 / D ** 0.5)
+
+    def cascade():
+        for l in range(layers):
+            P.paged_attention_decode_cascade(out[l], q[l], K[l], V[l], bt, cl, scale, 4, mem, pb,
+                                             mpl, mcl, part, ws_c)
+
+    def plain():
+        for l in range(layers):
+            P.paged_attention_decode_splitkv(out[l], q[l], K[l], V[l], bt, cl, scale, 4, mcl,
+                                             part, ws_p)
+    ms_c = time_steps(torch, graph_of(torch, cascade).replay, steps, warmup)
+    ms_p = time_steps(torch, graph_of(torch, plain).replay, steps, warmup)
+    logical = int(lens.sum()) * Hkv * D * 4                      # K+V bytes attended
+    read = (8 * 4096 + int((lens - 4096).sum())) * Hkv * D * 4   # each shared block once
+    us_c, us_p = ms_c * 1e3 / layers, ms_p * 1e3 / layers
+    return {"us_per_layer": round(us_c, 3), "plain_splitkv_us_per_layer": round(us_p, 3),
+            "speedup_vs_plain": round(us_p / us_c, 3),
+            "kv_bytes_attended_per_layer": logical, "kv_bytes_read_per_layer": read,
+            "kv_stream_gbs": round(read / (us_c * 1e-6) / 1e9, 2),
+            "pct_of_hbm_peak": round(100 * read / (us_c * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+            "attended_gbs": round(logical / (us_c * 1e-6) / 1e9, 2),
+            "layers": layers, "kv_format": "bf16",
+            "form": "cascade (prefix pass + suffix pass + merge) vs plain split-KV, partition 512, "
+                    "HIP graph"}
+
+
 def copy_calibration(torch):
     """A plain device copy of known size: 1 GiB read + 1 GiB written per launch.
     rocprofv3's FETCH_SIZE / WRITE_SIZE for these launches give the scale
@@ -461,6 +511,10 @@ def main():
             result["other_workloads"][name] = other_workload(name, P, W, torch, args.steps,
                                                              args.warmup)
             torch.cuda.empty_cache()
+        log("timing cascade")
+        result["other_workloads"]["cascade_system_prompt"] = cascade_workload(
+            P, W, torch, args.steps, args.warmup)
+        torch.cuda.empty_cache()
         log("timing gather_kv_cache")
         result["other_workloads"]["gather_llama8b_batch"] = gather_workload(P, W, torch,
                                                                             args.steps, args.warmup)

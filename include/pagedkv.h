@@ -244,6 +244,48 @@ int paged_attention_decode_splitkv_window(void* out, int out_dtype, const void* 
                                           size_t workspace_bytes, void* stream);
 
 /*
+ * paged_attention_decode_cascade — split-KV decode for batches whose
+ * sequences share whole-block prefixes in groups (mlxcel "KV Cache", Paged
+ * Decode Storage and Kernels: cascade attention for groups that share a
+ * sufficiently long whole-page prefix).  The result is that of
+ * paged_attention_decode_splitkv (up to fp32 summation order); the shared
+ * blocks are read once per group instead of once per member:
+ *   1. prefix pass: for group g, the first group_prefix_blocks[g] blocks of
+ *      the table of its first member group_members[g][0] are attended by the
+ *      query rows of every member at once (the rows are stacked in one tile,
+ *      so group_size * gqa_factor * q_len <= 16); each row keeps its own
+ *      causal limit;
+ *   2. suffix pass: every sequence attends its positions from the end of its
+ *      group's prefix (from 0 outside every group);
+ *   3. the log-sum-exp merge of both passes' partials.
+ *   group_members: int32 [num_groups, group_size], device; sequence indices,
+ *                  -1 for an empty slot.  A sequence appears in at most one
+ *                  group; a group whose first slot is -1 is ignored.
+ *   group_prefix_blocks: int32 [num_groups], device; the members' first
+ *                  group_prefix_blocks[g] table entries must name the same
+ *                  blocks (only the first member's are read).
+ *   max_prefix_len: host bound on 16 * group_prefix_blocks[g] (grid size).
+ * Workspace: paged_attention_decode_cascade_workspace_size bytes (prefix and
+ * suffix partials side by side; contents on entry do not matter).  No window,
+ * no append form.  16-bit caches only.
+ */
+int paged_attention_decode_cascade_workspace_size(int batch, int q_len, int num_q_heads,
+                                                  int head_dim, int max_context_len,
+                                                  int max_prefix_len, int partition_size,
+                                                  size_t* out_bytes);
+
+int paged_attention_decode_cascade(void* out, int out_dtype, const void* query,
+                                   const void* key_cache, const void* value_cache, int kv_dtype,
+                                   const int32_t* block_tables, int max_blocks_per_seq,
+                                   const int32_t* context_lens, int batch, int q_len,
+                                   int num_q_heads, int gqa_factor, int head_dim, int block_size,
+                                   int64_t num_blocks, float scale, const int32_t* group_members,
+                                   const int32_t* group_prefix_blocks, int num_groups,
+                                   int group_size, int max_prefix_len, int max_context_len,
+                                   int partition_size, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/*
  * paged_attention_decode_append / paged_attention_decode_splitkv_append —
  * the decode step with the slot write folded into the attention launch
  * (mlxcel "KV Cache", Attention Dispatch and In-Place Decode Writes: the new

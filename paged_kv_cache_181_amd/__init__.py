@@ -20,6 +20,7 @@ _EXPORTS = (
     "paged_attention_decode_splitkv_merge", "paged_attention_decode_append",
     "paged_attention_decode_splitkv_append", "paged_attention_decode_splitkv_append_partials",
     "paged_attention_decode_window", "paged_attention_decode_splitkv_window", "gather_kv_cache",
+    "paged_attention_decode_cascade", "cascade_workspace_size",
 )
 
 __all__ = list(_EXPORTS)

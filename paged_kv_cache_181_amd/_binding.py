@@ -68,6 +68,9 @@ SIGNATURES = {
                                                        + [_i, _i, _p, _sz, _p], _i),
     "paged_attention_decode_window": (_ATTN + [_i, _p], _i),
     "gather_kv_cache": ([_p, _p, _i, _p, _i, _p, _i, _i, _p, _p, _i64, _i, _i, _i, _i64, _p], _i),
+    "paged_attention_decode_cascade_workspace_size": ([_i, _i, _i, _i, _i, _i, _i,
+                                                       ctypes.POINTER(_sz)], _i),
+    "paged_attention_decode_cascade": (_ATTN + [_p, _p, _i, _i, _i, _i, _i, _p, _sz, _p], _i),
     "paged_attention_decode_splitkv_window": (_ATTN + [_i, _i, _i, _p, _sz, _p], _i),
 }
 for _name, (_args, _res) in SIGNATURES.items():
@@ -335,6 +338,43 @@ def gather_kv_cache(key_cache, value_cache, block_tables, cu_seq_lens, max_seq_l
         block_tables.shape[1], _ptr(cu_seq_lens), block_tables.shape[0], int(max_seq_len),
         _ptr(key_out), _ptr(value_out), key_out.shape[0], key_cache.shape[2], key_cache.shape[3],
         key_cache.shape[1], key_cache.shape[0], _stream(dev)))
+
+
+def cascade_workspace_size(batch, q_len, num_q_heads, head_dim, max_context_len, max_prefix_len,
+                           partition_size) -> int:
+    n = _sz(0)
+    _check(lib.paged_attention_decode_cascade_workspace_size(
+        batch, q_len, num_q_heads, head_dim, max_context_len, max_prefix_len, partition_size,
+        ctypes.byref(n)))
+    return n.value
+
+
+def paged_attention_decode_cascade(out, query, key_cache, value_cache, block_tables, context_lens,
+                                   scale, gqa_factor, group_members, group_prefix_blocks,
+                                   max_prefix_len, max_context_len, partition_size, workspace):
+    """Split-KV decode reading each group's shared prefix once (prefix pass,
+    suffix pass, merge).  group_members: int32 [groups, group_size];
+    group_prefix_blocks: int32 [groups]."""
+    torch = _torch()
+    dev = _dev(out, query, key_cache, value_cache, block_tables, context_lens, group_members,
+               group_prefix_blocks, workspace)
+    B, Q, Hq, D = _attn_common(out, query, block_tables, context_lens, gqa_factor)
+    _expect(key_cache.shape == value_cache.shape and key_cache.shape[2:] == (Hq // gqa_factor, D),
+            "caches must be [NB, 16, Hq/G, D]")
+    _expect(query.dtype == key_cache.dtype == value_cache.dtype, "query/cache dtype mismatch")
+    _expect(group_members.dtype == torch.int32 and group_members.dim() == 2,
+            "group_members must be int32 [groups, group_size]")
+    _expect(group_prefix_blocks.dtype == torch.int32
+            and group_prefix_blocks.shape == (group_members.shape[0],),
+            "group_prefix_blocks must be int32 [groups]")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.paged_attention_decode_cascade(
+        _ptr(out), _dtype_code(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+        _dtype_code(key_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        B, Q, Hq, gqa_factor, D, key_cache.shape[1], key_cache.shape[0], float(scale),
+        _ptr(group_members), _ptr(group_prefix_blocks), group_members.shape[0],
+        group_members.shape[1], int(max_prefix_len), int(max_context_len), int(partition_size),
+        _ptr(workspace), nbytes, _stream(dev)))
 
 
 def _k8v4_check(query, gqa_factor, k_cache, k_scale, v_cache, v_scale, v_zero):

@@ -129,6 +129,8 @@ int setup_split(pkv::AttnArgs& a, int head_dim, int max_context_len, int partiti
                 workspace_bytes, need);
   const int64_t rows = (int64_t)a.batch * a.q_len * a.num_q_heads;
   a.num_parts = (int)parts;
+  a.ws_parts = (int)parts;
+  a.part_base = 0;
   a.part_blocks = partition_size / 16;
   a.ws_o = (float*)workspace;
   a.ws_m = a.ws_o + rows * parts * head_dim;
@@ -344,6 +346,97 @@ int paged_attention_decode_splitkv_window(void* out, int out_dtype, const void* 
                        "paged_attention_decode_splitkv_window");
 }
 
+int paged_attention_decode_cascade_workspace_size(int batch, int q_len, int num_q_heads,
+                                                  int head_dim, int max_context_len,
+                                                  int max_prefix_len, int partition_size,
+                                                  size_t* out_bytes) {
+  if (!out_bytes) return fail(PKV_ERR_NULL, "out_bytes is NULL");
+  if (max_prefix_len < 0) return fail(PKV_ERR_SHAPE, "max_prefix_len must be >= 0");
+  int64_t p_pre = 0, p_suf = 0;
+  size_t b_pre = 0, b_suf = 0;
+  int rc = split_geometry(batch, q_len, num_q_heads, head_dim, max_prefix_len, partition_size,
+                          p_pre, b_pre);
+  if (rc) return rc;
+  rc = split_geometry(batch, q_len, num_q_heads, head_dim, max_context_len, partition_size,
+                      p_suf, b_suf);
+  if (rc) return rc;
+  *out_bytes = b_pre + b_suf;
+  return ok();
+}
+
+int paged_attention_decode_cascade(void* out, int out_dtype, const void* query,
+                                   const void* key_cache, const void* value_cache, int kv_dtype,
+                                   const int32_t* block_tables, int max_blocks_per_seq,
+                                   const int32_t* context_lens, int batch, int q_len,
+                                   int num_q_heads, int gqa_factor, int head_dim, int block_size,
+                                   int64_t num_blocks, float scale, const int32_t* group_members,
+                                   const int32_t* group_prefix_blocks, int num_groups,
+                                   int group_size, int max_prefix_len, int max_context_len,
+                                   int partition_size, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  if (kv_dtype != PKV_F16 && kv_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "kv_dtype must be PKV_F16 or PKV_BF16");
+  if (num_groups < 0 || group_size < 0 || max_prefix_len < 0)
+    return fail(PKV_ERR_SHAPE, "num_groups, group_size and max_prefix_len must be >= 0");
+  if (num_groups > 65535) return fail(PKV_ERR_UNSUPPORTED, "too many groups");
+  if (num_groups > 0 && ((int64_t)group_size * gqa_factor * q_len > 16 || group_size == 0))
+    return fail(PKV_ERR_UNSUPPORTED,
+                "group_size * gqa_factor * q_len must be between 1 and 16 (got %lld)",
+                (long long)group_size * gqa_factor * q_len);
+  pkv::AttnArgs a{};
+  int rc = check_attention(out, out_dtype, query, key_cache, value_cache, block_tables,
+                           max_blocks_per_seq, context_lens, batch, q_len, num_q_heads, gqa_factor,
+                           head_dim, block_size, num_blocks, scale, a);
+  if (rc) return rc;
+  if (batch == 0) return ok();
+  if (num_groups > 0 && (!group_members || !group_prefix_blocks))
+    return fail(PKV_ERR_NULL, "group arrays are NULL");
+  int64_t p_pre = 0, p_suf = 0;
+  size_t b_pre = 0, b_suf = 0;
+  rc = split_geometry(batch, q_len, num_q_heads, head_dim, max_prefix_len, partition_size,
+                      p_pre, b_pre);
+  if (rc) return rc;
+  rc = split_geometry(batch, q_len, num_q_heads, head_dim, max_context_len, partition_size,
+                      p_suf, b_suf);
+  if (rc) return rc;
+  if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(PKV_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (workspace_bytes < b_pre + b_suf)
+    return fail(PKV_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed",
+                workspace_bytes, b_pre + b_suf);
+  const int64_t rows = (int64_t)batch * q_len * num_q_heads;
+  const int64_t total = p_pre + p_suf;
+  a.ws_parts = (int)total;
+  a.part_blocks = partition_size / 16;
+  a.ws_o = (float*)workspace;
+  a.ws_m = a.ws_o + rows * total * head_dim;
+  a.ws_l = a.ws_m + rows * total;
+  a.grp_members = group_members;
+  a.grp_prefix = group_prefix_blocks;
+  a.num_groups = num_groups;
+  a.group_size = group_size;
+  hipError_t e = hipSuccess;
+  // 1. the shared prefixes, once per group (slots 0 .. p_pre-1; groups absent: none)
+  if (num_groups > 0) {
+    pkv::AttnArgs pre = a;
+    pre.mode = 1;
+    pre.num_parts = (int)p_pre;
+    pre.part_base = 0;
+    e = pkv::launch_attention(pre, kv_dtype, kv_dtype, head_dim, (hipStream_t)stream,
+                              pkv::STAGE_PARTIALS);
+    if (e != hipSuccess) return launch_result(e, "paged_attention_decode_cascade (prefix)");
+  }
+  // 2. every sequence past its group's prefix (slots p_pre ..), marking the
+  //    prefix slots of sequences outside every group empty; 3. the merge
+  pkv::AttnArgs suf = a;
+  suf.mode = 2;
+  suf.num_parts = (int)p_suf;
+  suf.part_base = (int)p_pre;
+  return launch_result(pkv::launch_attention(suf, kv_dtype, kv_dtype, head_dim,
+                                             (hipStream_t)stream),
+                       "paged_attention_decode_cascade");
+}
+
 int paged_attention_decode_append(void* out, int out_dtype, const void* query,
                                   const void* new_key, const void* new_value, void* key_cache,
                                   void* value_cache, int kv_dtype, const int32_t* block_tables,
@@ -557,6 +650,7 @@ int paged_attention_decode_splitkv_merge(void* out, int out_dtype, int batch, in
   a.num_q_heads = num_q_heads;
   const int64_t rows = (int64_t)batch * q_len * num_q_heads;
   a.num_parts = (int)parts;
+  a.ws_parts = (int)parts;
   a.part_blocks = partition_size / 16;
   a.ws_o = (float*)workspace;
   a.ws_m = a.ws_o + rows * parts * head_dim;

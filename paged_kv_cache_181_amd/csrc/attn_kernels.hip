@@ -227,7 +227,7 @@ __device__ __forceinline__ u2 lds_read_tr16(const unsigned char* p) {
 // then at most 2^8, well inside fp16/bf16 range.
 constexpr float kRescaleSlack = 8.f;
 
-template <Fmt KV, Fmt QT, int D, int RT>
+template <Fmt KV, Fmt QT, int D, int RT, bool PREFIX>
 __global__ __launch_bounds__((Shape<KV, RT>::NW * kWave), (Shape<KV, RT>::WAVES_PER_SIMD))
 void attn_partition_kernel(const AttnArgs a) {
   using MM = Mma<QT>;
@@ -247,6 +247,22 @@ void attn_partition_kernel(const AttnArgs a) {
   const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int Q = a.q_len, G = a.gqa, GQ = G * Q, Hq = a.num_q_heads;
   const bool split = a.ws_o != nullptr;
+  // Cascade passes over shared whole-block prefixes.  Prefix pass (PREFIX,
+  // mode 1): b is a group; its S members' rows are stacked in the tile
+  // (member m's row iq*G + hl at tile row m*GQ + iq*G + hl), so the shared
+  // blocks are read once for all of them.  Suffix pass (mode 2): b is a
+  // sequence whose blocks covered by its group's prefix are skipped.
+  // Mode 0: plain.
+  const int mode = PREFIX ? 1 : a.mode;
+  const int S = PREFIX ? a.group_size : 1;
+  const int GQT = S * GQ;                                   // tile rows that belong to sequences
+  // output (= query) row of tile row rr < GQT, or -1 for an empty member slot
+  auto orow_of = [&](int rr) -> int64_t {
+    const int m = rr / GQ, rq = rr - m * GQ;
+    const int bm = PREFIX ? a.grp_members[(int64_t)b * S + m] : b;
+    return bm < 0 ? -1 : ((int64_t)bm * Q + rq / G) * Hq + g * G + rq % G;
+  };
+  const int64_t wsp = a.ws_parts;                           // partition slots per row
 
   // ---- loads that do not depend on the sequence length go out first and
   // together: the table entries of this wave's first blocks, this wave's copy
@@ -256,8 +272,10 @@ void attn_partition_kernel(const AttnArgs a) {
   // j of a 64-entry chunk of the run, picked out later with readlane, so no
   // table load sits between the K/V loads of consecutive blocks.  Nothing
   // waits on another wave before the first K/V loads.
-  // the sequence's table row; entries past max_blocks read as 0 (never used)
-  const auto btr = span_rsrc(a.block_tables + (int64_t)b * a.max_blocks,
+  // the sequence's table row (a group's: its first member's); entries past
+  // max_blocks read as 0 (never used)
+  const int tab_b = PREFIX ? a.grp_members[(int64_t)b * S] : b;
+  const auto btr = span_rsrc(a.block_tables + (int64_t)max(tab_b, 0) * a.max_blocks,
                              (uint32_t)a.max_blocks * 4u);
   const int bb_guess = p * a.part_blocks;       // the partition's first block without a window
   int per = (a.part_blocks + NW - 1) / NW;
@@ -274,12 +292,13 @@ void attn_partition_kernel(const AttnArgs a) {
     const int idx = lane + u * kWave;
     const int r = idx / (D / 8), c8 = idx % (D / 8);
     qv[u] = u4{0u, 0u, 0u, 0u};
-    if (idx < QCW && r < GQ) {
-      const int h = g * G + r % G;
-      qv[u] = *(const u4*)((const uint16_t*)a.q + (((int64_t)b * Q + r / G) * Hq + h) * D + 8 * c8);
+    if (idx < QCW && r < GQT) {
+      const int64_t qr = orow_of(r);
+      if (qr >= 0) qv[u] = *(const u4*)((const uint16_t*)a.q + qr * D + 8 * c8);
     }
   }
-  int L = a.context_lens[b];
+  // the length the block loop covers: the sequence's, or a group's shared prefix
+  int L = PREFIX ? (tab_b >= 0 ? a.grp_prefix[b] * kBlock : 0) : a.context_lens[b];
   L = min(max(L, 0), a.max_blocks * kBlock);
   // Append form: the q_len new tokens (positions L-Q .. L-1) come from the
   // new K/V rows, not the cache; the partition holding position L-1 attends
@@ -291,7 +310,31 @@ void attn_partition_kernel(const AttnArgs a) {
   // L-Q+i, so nothing before lo0 (row 0's first position) is read at all,
   // and partitions are counted from lo0's block (the grid covers the window).
   const int W = a.window;
-  const int lo0 = W > 0 ? max(L - Q - W + 1, 0) : 0;
+  // suffix pass: the blocks of b's group prefix (a group counts if its first
+  // member slot names a sequence) are the prefix pass's; start after them
+  int pre_b = 0;
+  if (mode == 2) {
+    const int total = a.num_groups * a.group_size;
+    for (int base = 0; base < total; base += kWave) {
+      const int idx = base + lane;
+      const bool hit = idx < total && a.grp_members[idx] == b &&
+                       a.grp_members[(idx / a.group_size) * a.group_size] >= 0;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(hit);
+      if (bal) {
+        pre_b = a.grp_prefix[(base + __builtin_ctzll(bal)) / a.group_size];
+        break;
+      }
+    }
+    pre_b = min(max(pre_b, 0), nblk);
+    if (split && p == 0 && pre_b == 0) {      // no group: its prefix slots are empty
+      for (int idx = threadIdx.x; idx < GQ * a.part_base; idx += NW * kWave) {
+        const int64_t pi = orow_of(idx % GQ) * wsp + idx / GQ;
+        a.ws_m[pi] = kNegInf;
+        a.ws_l[pi] = 0.f;
+      }
+    }
+  }
+  const int lo0 = mode == 2 ? pre_b * kBlock : W > 0 ? max(L - Q - W + 1, 0) : 0;
   const int sb = lo0 / kBlock;
   const int bb = sb + bb_guess;                             // the partition's first block
   const int p_new = append && L > 0
@@ -301,8 +344,10 @@ void attn_partition_kernel(const AttnArgs a) {
   if (split && b0 >= be && p != p_new) {                    // partition with nothing to read:
     // mark it empty (max -inf, sum 0) so the merge can read every partition
     // without first reading the sequence length
-    for (int rr = threadIdx.x; rr < GQ; rr += NW * kWave) {
-      const int64_t pi = (((int64_t)b * Q + rr / G) * Hq + g * G + rr % G) * a.num_parts + p;
+    for (int rr = threadIdx.x; rr < GQT; rr += NW * kWave) {
+      const int64_t orow = orow_of(rr);
+      if (orow < 0) continue;
+      const int64_t pi = orow * wsp + a.part_base + p;
       a.ws_m[pi] = kNegInf;
       a.ws_l[pi] = 0.f;
     }
@@ -319,12 +364,20 @@ void attn_partition_kernel(const AttnArgs a) {
   const int w0 = b0 + w * per;                              // first block of this wave's run
   const int nmine = max(0, min(per, be - w0));
 
-  // the query row this lane owns: rho = iq * G + hl (lanes past G*q_len
-  // compute a copy of a real row; their results are never written)
-  const bool row_ok = rho < GQ;
-  const int iq = row_ok ? rho / G : 0;
-  const int nvis = row_ok ? (L - Q + iq + 1) : L;           // visible positions of the row
-  const int full_lim = L - Q + 1;                           // every row sees j < full_lim
+  // the query row this lane owns: rho = iq * G + hl, or in the prefix pass
+  // member rho / GQ's row (rho % GQ) (lanes past the rows compute a copy of
+  // a real row; their results are never written)
+  int row_len = L;                                          // the row's sequence length
+  bool row_ok = rho < GQT;
+  if (PREFIX && row_ok) {
+    const int bm = a.grp_members[(int64_t)b * S + rho / GQ];
+    row_ok = bm >= 0;
+    row_len = row_ok ? min(max(a.context_lens[bm], 0), a.max_blocks * kBlock) : 0;
+  }
+  const int iq = row_ok ? (rho % GQ) / G : 0;
+  const int nvis = row_ok ? (row_len - Q + iq + 1) : L;     // visible positions of the row
+  // every row sees j < full_lim (the prefix pass masks every tile instead)
+  const int full_lim = PREFIX ? -(1 << 30) : L - Q + 1;
   const int lo_row = W > 0 && row_ok ? max(L - Q + iq - W + 1, 0) : lo0;   // window start
   const int lo_max = W > 0 ? max(L - W, 0) : 0;             // every row sees j >= lo_max
 
@@ -599,7 +652,7 @@ void attn_partition_kernel(const AttnArgs a) {
   // ---- merge the NW wavefronts of this workgroup (LDS reused)
   __syncthreads();
   float* mo = (float*)smem;
-  if (rho < RT && row_ok) {
+  if (rho < RT && rho < GQT) {
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
@@ -610,7 +663,7 @@ void attn_partition_kernel(const AttnArgs a) {
     ml_s[w][rho] = l_run;
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < GQ * D; idx += NW * kWave) {
+  for (int idx = threadIdx.x; idx < GQT * D; idx += NW * kWave) {
     const int rr = idx / D, d = idx % D;
     float M = kNegInf;
 #pragma unroll
@@ -623,9 +676,10 @@ void attn_partition_kernel(const AttnArgs a) {
       num += e * mo[(ww * RT + rr) * D + d];
       den += e * ml_s[ww][rr];
     }
-    const int64_t orow = ((int64_t)b * Q + rr / G) * Hq + g * G + rr % G;
+    const int64_t orow = orow_of(rr);
+    if (orow < 0) continue;
     if (split) {
-      const int64_t pi = orow * a.num_parts + p;
+      const int64_t pi = orow * wsp + a.part_base + p;
       a.ws_o[pi * D + d] = num;
       if (d == 0) {
         a.ws_m[pi] = M;
@@ -652,10 +706,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
   const int64_t row = blockIdx.x;
   const int t = threadIdx.x;
   // every partition of the grid holds a partial or an empty marker (max -inf)
-  const int np = a.num_parts;
-  const float* wm = a.ws_m + row * a.num_parts;
-  const float* wl = a.ws_l + row * a.num_parts;
-  const float* wo = a.ws_o + row * a.num_parts * D;
+  const int np = a.ws_parts;
+  const float* wm = a.ws_m + row * np;
+  const float* wl = a.ws_l + row * np;
+  const float* wo = a.ws_o + row * np * D;
 
   const int c = t % NC, grp = t / NC;
   float m_t = kNegInf, den = 0.f;
@@ -722,12 +776,27 @@ static hipError_t launch_merge(const AttnArgs& a, hipStream_t stream) {
 template <Fmt KV, Fmt QT, int D>
 static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream, int stage) {
   if (stage != STAGE_MERGE) {
-    const dim3 grid((unsigned)a.num_parts, (unsigned)a.num_kv_heads, (unsigned)a.batch);
-    if (a.gqa * a.q_len <= 4) {
-      hipLaunchKernelGGL((attn_partition_kernel<KV, QT, D, 4>), grid,
+    const int rows = (a.mode == 1 ? a.group_size : 1) * a.gqa * a.q_len;
+    const dim3 grid((unsigned)a.num_parts, (unsigned)a.num_kv_heads,
+                    (unsigned)(a.mode == 1 ? a.num_groups : a.batch));
+    if constexpr (KV != Fmt::K8V4) {
+      if (a.mode == 1) {                 // cascade prefix pass: its own instantiation
+        if (rows <= 4)
+          hipLaunchKernelGGL((attn_partition_kernel<KV, QT, D, 4, true>), grid,
+                             dim3(Shape<KV, 4>::NW * kWave), 0, stream, a);
+        else
+          hipLaunchKernelGGL((attn_partition_kernel<KV, QT, D, 16, true>), grid,
+                             dim3(Shape<KV, 16>::NW * kWave), 0, stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || stage == STAGE_PARTIALS) return e;
+        return launch_merge<D>(a, stream);
+      }
+    }
+    if (rows <= 4) {
+      hipLaunchKernelGGL((attn_partition_kernel<KV, QT, D, 4, false>), grid,
                          dim3(Shape<KV, 4>::NW * kWave), 0, stream, a);
     } else {
-      hipLaunchKernelGGL((attn_partition_kernel<KV, QT, D, 16>), grid,
+      hipLaunchKernelGGL((attn_partition_kernel<KV, QT, D, 16, false>), grid,
                          dim3(Shape<KV, 16>::NW * kWave), 0, stream, a);
     }
     hipError_t e = hipGetLastError();

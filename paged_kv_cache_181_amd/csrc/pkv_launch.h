@@ -47,6 +47,12 @@ struct AttnArgs {
   const void* new_k;             // append form (16-bit only): [B*Q, Hkv, D] new rows, else NULL
   const void* new_v;             // append form: [B*Q, Hkv, D]
   int window;                    // sliding window in positions (0: the whole context)
+  int ws_parts;                  // partition slots per row in the workspace
+  int part_base;                 // first slot this launch's partitions write
+  int mode;                      // 0 plain, 1 cascade prefix pass, 2 cascade suffix pass
+  const int32_t* grp_members;    // cascade: [num_groups, group_size] sequence ids (-1: empty)
+  const int32_t* grp_prefix;     // cascade: [num_groups] shared whole blocks
+  int num_groups, group_size;
 };
 
 // kv_fmt: 0 f16, 1 bf16, 3 k8v4; q_fmt: 0 f16, 1 bf16 (must equal kv_fmt unless k8v4).

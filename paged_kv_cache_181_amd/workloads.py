@@ -225,6 +225,75 @@ def k8v4(seed: int = 5, batch: int = 16, length: int = 8192) -> PagedCase:
                      head_dim=128, fmt="f16", lengths=[length] * batch, num_blocks=nb)
 
 
+def shared_prefix_layout(rng, groups: int, group_size: int, prefix_len: int, suffix_lo: int,
+                         suffix_hi: int):
+    """Lengths and tables of a shared-prefix batch (draws: suffix lengths, then
+    the pool permutation).  Returns (lens int64 [B], tables int32 [B, mb],
+    num_blocks, used block ids, group_members [groups, group_size],
+    prefix_blocks [groups])."""
+    if prefix_len % BLOCK_SIZE:
+        raise ValueError("the shared prefix is whole blocks")
+    batch = groups * group_size
+    suffix = rng.integers(suffix_lo, suffix_hi + 1, size=batch).astype(np.int64)
+    lens = prefix_len + suffix
+    pre_blocks = prefix_len // BLOCK_SIZE
+    own = (suffix + BLOCK_SIZE - 1) // BLOCK_SIZE
+    nb = groups * pre_blocks + int(own.sum()) + 8
+    perm = rng.permutation(nb).astype(np.int32)
+    mb = int(pre_blocks + own.max())
+    tables = np.full((batch, mb), -1, dtype=np.int32)
+    pos = 0
+    group_blocks = []
+    for _ in range(groups):
+        group_blocks.append(perm[pos:pos + pre_blocks])
+        pos += pre_blocks
+    for b in range(batch):
+        tables[b, :pre_blocks] = group_blocks[b // group_size]
+        tables[b, pre_blocks:pre_blocks + own[b]] = perm[pos:pos + own[b]]
+        pos += int(own[b])
+    used = np.concatenate(group_blocks + [tables[b, pre_blocks:pre_blocks + own[b]]
+                                          for b in range(batch)])
+    members = np.arange(batch, dtype=np.int32).reshape(groups, group_size)
+    return lens, tables, nb, used, members, np.full(groups, pre_blocks, dtype=np.int32)
+
+
+def shared_prefix(seed: int = 6, groups: int = 8, group_size: int = 4, prefix_len: int = 4096,
+                  suffix_lo: int = 64, suffix_hi: int = 1024, num_q_heads: int = 32,
+                  num_kv_heads: int = 8, head_dim: int = 128, fmt: str = "bf16",
+                  q_len: int = 1) -> PagedCase:
+    """Batches whose sequences share a whole-block prefix in groups (a common
+    system prompt): ``groups`` groups of ``group_size`` sequences; the members
+    of a group point their first ``prefix_len / 16`` table entries at the same
+    physical blocks, then each has its own suffix of uniform length in
+    [suffix_lo, suffix_hi] (this step's tokens included).  Draw order:
+    suffix lengths, pool permutation, K, V, query, new K, new V.
+    ``extra`` holds ``group_members`` int32 [groups, group_size] and
+    ``prefix_blocks`` int32 [groups]."""
+    rng = rng_for(seed)
+    lens, tables, nb, used, members, pre = shared_prefix_layout(rng, groups, group_size,
+                                                                prefix_len, suffix_lo, suffix_hi)
+    batch = groups * group_size
+    shape = (nb, BLOCK_SIZE, num_kv_heads, head_dim)
+    kc = np.zeros(shape, dtype=np.uint16)
+    vc = np.zeros(shape, dtype=np.uint16)
+    for pool in (kc, vc):
+        for st in range(0, len(used), 2048):
+            ids = used[st:st + 2048]
+            pool[ids] = normal_bits(rng, (len(ids),) + shape[1:], fmt)
+    query = normal_bits(rng, (batch, q_len, num_q_heads, head_dim), fmt)
+    slots = np.asarray([slot_of(tables, b, int(lens[b]) - q_len + i)
+                        for b in range(batch) for i in range(q_len)], dtype=np.int64)
+    new_key = normal_bits(rng, (batch * q_len, num_kv_heads, head_dim), fmt)
+    new_value = normal_bits(rng, (batch * q_len, num_kv_heads, head_dim), fmt)
+    return PagedCase(
+        name="shared_prefix", batch=batch, q_len=q_len, num_q_heads=num_q_heads,
+        num_kv_heads=num_kv_heads, head_dim=head_dim, fmt=fmt, num_blocks=nb,
+        context_lens=lens.astype(np.int32), block_tables=tables, key_cache=kc, value_cache=vc,
+        query=query, new_key=new_key, new_value=new_value, slot_mapping=slots,
+        scale=float(np.float32(1.0 / np.sqrt(head_dim))),
+        extra={"group_members": members, "prefix_blocks": pre})
+
+
 def layout_of(name: str, seed: int) -> tuple:
     """(Layout, batch, q_len, Hq, Hkv, D, fmt) of a named workload, drawing only
     the lengths and tables (same draws as the full builder up to that point)."""
@@ -253,6 +322,7 @@ WORKLOADS = {
     "long32k": long32k,
     "spec_verify": spec_verify,
     "k8v4": k8v4,
+    "shared_prefix": shared_prefix,
 }
 
 

@@ -212,3 +212,25 @@ def test_gather_argument_errors(P):
     for i in (0, 1, 3, 5, 8, 9):
         empty[i] = None
     assert lib.gather_kv_cache(*empty, None) == 0
+
+
+def test_cascade_workspace_and_errors(P):
+    # rows * (prefix partitions + suffix partitions) * (D + 2) * 4
+    assert P.cascade_workspace_size(32, 1, 32, 128, 5120, 4096, 512) == 32 * 32 * (8 + 10) * 130 * 4
+    assert P.cascade_workspace_size(4, 2, 8, 64, 100, 0, 16) == 4 * 2 * 8 * (1 + 7) * 66 * 4
+    lib = P.lib
+    base = [FAKE, 0, FAKE, FAKE, FAKE, 0, FAKE, 8, FAKE, 8, 1, 32, 4, 128, 16, 64, 0.1]
+    #        members, prefix, groups, size, max_prefix, max_ctx, psize, ws, bytes
+    ok_tail = [FAKE, FAKE, 2, 4, 64, 128, 512, FAKE, 1 << 30]
+    bad = ok_tail.copy()
+    bad[3] = 5                                        # 5 * 4 * 1 rows > 16
+    assert lib.paged_attention_decode_cascade(*base, *bad, None) == -3
+    bad = ok_tail.copy()
+    bad[0] = None
+    assert lib.paged_attention_decode_cascade(*base, *bad, None) == -1
+    bad = ok_tail.copy()
+    bad[8] = 64
+    assert lib.paged_attention_decode_cascade(*base, *bad, None) == -4
+    bad = ok_tail.copy()
+    bad[4] = -16
+    assert lib.paged_attention_decode_cascade(*base, *bad, None) == -2

@@ -704,3 +704,68 @@ def test_gather_then_write_round_trip(P):
     used = np.unique(slots)
     kb = dev_to_bits(k).reshape(-1, *case.key_cache.shape[2:])
     assert np.array_equal(kb[used], case.key_cache.reshape(-1, *case.key_cache.shape[2:])[used])
+
+
+# ------------------------------------------------------------------ cascade (shared prefixes)
+
+def run_cascade(P, dc, members, prefix_blocks, *, psize=512, out_dtype=torch.float32):
+    c = dc.case
+    B, Q, Hq, D = dc.q.shape
+    mcl = int(dc.cl.max().item())
+    mpl = int(np.max(prefix_blocks)) * 16 if len(prefix_blocks) else 0
+    n = P.cascade_workspace_size(B, Q, Hq, D, mcl, mpl, psize)
+    ws = torch.full((n // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    out = torch.full(dc.q.shape, float("nan"), dtype=out_dtype, device="cuda")
+    P.paged_attention_decode_cascade(out, dc.q, dc.k, dc.v, dc.bt, dc.cl, c.scale, c.gqa_factor,
+                                     torch.from_numpy(np.asarray(members, np.int32)).cuda(),
+                                     torch.from_numpy(np.asarray(prefix_blocks, np.int32)).cuda(),
+                                     mpl, mcl, psize, ws)
+    torch.cuda.synchronize()
+    return out
+
+
+CASCADE_CASES = {
+    "small_g3x4": lambda: W.shared_prefix(seed=140, groups=3, group_size=4, prefix_len=64,
+                                          suffix_lo=1, suffix_hi=40, num_q_heads=8,
+                                          num_kv_heads=2, head_dim=64, fmt="f16"),
+    "q2_g4x2": lambda: W.shared_prefix(seed=141, groups=4, group_size=2, prefix_len=96,
+                                       suffix_lo=2, suffix_hi=70, num_q_heads=16,
+                                       num_kv_heads=4, head_dim=128, fmt="bf16", q_len=2),
+    "system_prompt": lambda: W.shared_prefix(seed=6),
+}
+
+
+@pytest.mark.parametrize("name", list(CASCADE_CASES))
+@pytest.mark.parametrize("psize", [512, 32])
+def test_cascade_matches_oracle(P, name, psize):
+    case = CASCADE_CASES[name]()
+    ref = oracle_decode(case)
+    dc = DevCase(case)
+    out = run_cascade(P, dc, case.extra["group_members"], case.extra["prefix_blocks"], psize=psize)
+    err = max_err(out, ref)
+    assert err <= 2e-4, f"{name}: fp32-out max abs err {err}"
+    plain = run_decode(P, dc, split=True, partition_size=psize)
+    assert (out - plain).abs().max().item() <= 1e-5
+
+
+def test_cascade_partial_groups_and_outsiders(P):
+    """Empty member slots, sequences in no group, a group whose first slot is
+    empty (ignored), and a member shorter than the shared prefix."""
+    case = W.shared_prefix(seed=142, groups=3, group_size=4, prefix_len=64, suffix_lo=1,
+                           suffix_hi=40, num_q_heads=8, num_kv_heads=2, head_dim=64, fmt="f16")
+    members = case.extra["group_members"].copy()
+    members[0, 3] = -1                 # sequence 3 outside every group
+    members[2, 0] = -1                 # group 2 ignored: 9, 10, 11 attend on their own
+    case.context_lens[1] = 40          # shorter than the 64-token shared prefix
+    ref = oracle_decode(case)
+    dc = DevCase(case)
+    for psize in (512, 32, 16):
+        out = run_cascade(P, dc, members, case.extra["prefix_blocks"], psize=psize)
+        assert max_err(out, ref) <= 2e-4, psize
+
+
+def test_cascade_without_groups_is_plain_split(P):
+    case, ref = get_case("small_bf16_d128_g4")
+    dc = DevCase(case)
+    out = run_cascade(P, dc, np.zeros((0, 1), np.int32), np.zeros(0, np.int32), psize=32)
+    assert max_err(out, ref) <= 2e-4
