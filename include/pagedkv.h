@@ -286,6 +286,31 @@ int paged_attention_decode_cascade(void* out, int out_dtype, const void* query,
                                    void* stream);
 
 /*
+ * paged_attention_decode_splitkv_sparse_v — APPROXIMATE split-KV decode that
+ * skips reading V rows of negligible weight ("The KV Cache" (metalworking),
+ * arithmetic paragraph: sparse-V decode at long context is a KV-cache traffic
+ * deletion; the skip rule is not given there, this is the library's):
+ *   the V row of position j (one KV head) is read only if some query row of
+ *   that head has 2^(s_j - m) >= v_threshold, where s is the row's score in
+ *   log2 units and m the row's running maximum score including j's block;
+ *   skipped positions still count in the softmax sum.
+ * Guarantee: a skipped position weighs less than v_threshold times its row's
+ * largest weight, so |out - exact| <= sum over such positions of
+ * w_j |v_j| / sum_j w_j per element.  v_threshold = 0 reads every row (the
+ * exact result).  v_rows_read (device, nullable) is incremented by the
+ * number of (block, KV head, token) V rows read.  Same arguments, workspace
+ * and errors as paged_attention_decode_splitkv otherwise; v_threshold outside
+ * [0, 1) is PKV_ERR_SHAPE; needs gqa_factor * q_len <= 4 and a 16-bit cache.
+ */
+int paged_attention_decode_splitkv_sparse_v(
+    void* out, int out_dtype, const void* query, const void* key_cache, const void* value_cache,
+    int kv_dtype, const int32_t* block_tables, int max_blocks_per_seq,
+    const int32_t* context_lens, int batch, int q_len, int num_q_heads, int gqa_factor,
+    int head_dim, int block_size, int64_t num_blocks, float scale, float v_threshold,
+    unsigned long long* v_rows_read, int max_context_len, int partition_size, void* workspace,
+    size_t workspace_bytes, void* stream);
+
+/*
  * paged_attention_decode_append / paged_attention_decode_splitkv_append —
  * the decode step with the slot write folded into the attention launch
  * (mlxcel "KV Cache", Attention Dispatch and In-Place Decode Writes: the new

@@ -245,6 +245,56 @@ def _attend(qv, read_rows, num_blocks, hkv, block_tables, context_lens, scale,
 
 
 # ---------------------------------------------------------------------------
+# Sparse-V (approximate): the error bound its skip rule guarantees
+# ---------------------------------------------------------------------------
+
+def sparse_v_error_bound(query, key_cache, value_cache, block_tables, context_lens, scale,
+                         gqa_factor, fmt, threshold, block_size=BLOCK_SIZE):
+    """Elementwise bound on |sparse-V output - exact output|.
+
+    "The KV Cache" (metalworking), arithmetic paragraph: a sparse-V decode
+    path at 32K deletes KV-cache traffic; the rule for what it skips is not
+    stated.  Reading: the V row of position j is read only when some query
+    row of its KV head has weight ``w_ij >= threshold * w_i,max`` with
+    respect to that row's running maximum; skipped positions still count in
+    the softmax denominator.  Since a running maximum never exceeds the final
+    one, every skipped position has ``w_ij / max_j w_ij < threshold`` in the
+    exact weights, so for each output element
+
+        |o_sparse - o_exact| <= sum_{j : w_ij < threshold * max w_i} w_ij |v_jd| / sum_j w_ij.
+
+    Returns float64 ``[B, Q, Hq, D]`` of that right-hand side (0 when
+    ``threshold`` is 0).
+    """
+    qv = decode(query, fmt)
+    b_count, q_len, hq, d = qv.shape
+    hkv = key_cache.shape[2]
+    bt = np.asarray(block_tables)
+    out = np.zeros((b_count, q_len, hq, d), dtype=np.float64)
+    scale64 = float(np.float32(scale))
+    for b in range(b_count):
+        length = effective_length(int(context_lens[b]), bt.shape[1], block_size)
+        valid, blk, off = resolve_positions(bt[b], length, key_cache.shape[0], block_size)
+        keys = decode(key_cache[blk, off], fmt)
+        vals = decode(value_cache[blk, off], fmt)
+        for h in range(hq):
+            g = h // gqa_factor
+            for i in range(q_len):
+                n = min(visible_count(length, q_len, i), length)
+                if n <= 0:
+                    continue
+                mask = valid[:n]
+                if not mask.any():
+                    continue
+                s = scale64 * (keys[:n][mask][:, g, :] @ qv[b, i, h])
+                w = np.exp(s - s.max())
+                small = w < threshold
+                out[b, i, h] = (w[small][:, None] * np.abs(vals[:n][mask][small][:, g, :])).sum(0) \
+                    / w.sum()
+    return out
+
+
+# ---------------------------------------------------------------------------
 # gather_kv_cache: paged -> contiguous (the inverse of the slot scatter)
 # ---------------------------------------------------------------------------
 

@@ -71,6 +71,7 @@ SIGNATURES = {
     "paged_attention_decode_cascade_workspace_size": ([_i, _i, _i, _i, _i, _i, _i,
                                                        ctypes.POINTER(_sz)], _i),
     "paged_attention_decode_cascade": (_ATTN + [_p, _p, _i, _i, _i, _i, _i, _p, _sz, _p], _i),
+    "paged_attention_decode_splitkv_sparse_v": (_ATTN + [_f, _p, _i, _i, _p, _sz, _p], _i),
     "paged_attention_decode_splitkv_window": (_ATTN + [_i, _i, _i, _p, _sz, _p], _i),
 }
 for _name, (_args, _res) in SIGNATURES.items():
@@ -374,6 +375,31 @@ def paged_attention_decode_cascade(out, query, key_cache, value_cache, block_tab
         B, Q, Hq, gqa_factor, D, key_cache.shape[1], key_cache.shape[0], float(scale),
         _ptr(group_members), _ptr(group_prefix_blocks), group_members.shape[0],
         group_members.shape[1], int(max_prefix_len), int(max_context_len), int(partition_size),
+        _ptr(workspace), nbytes, _stream(dev)))
+
+
+def paged_attention_decode_splitkv_sparse_v(out, query, key_cache, value_cache, block_tables,
+                                            context_lens, scale, gqa_factor, v_threshold,
+                                            max_context_len, partition_size, workspace,
+                                            v_rows_read=None):
+    """Approximate split-KV decode that reads a V row only if some query row
+    weighs it at least ``v_threshold`` of its running maximum.  ``v_rows_read``
+    (int64 [1], optional) accumulates the number of V rows read."""
+    torch = _torch()
+    dev = _dev(out, query, key_cache, value_cache, block_tables, context_lens, workspace,
+               v_rows_read)
+    B, Q, Hq, D = _attn_common(out, query, block_tables, context_lens, gqa_factor)
+    _expect(key_cache.shape == value_cache.shape and key_cache.shape[2:] == (Hq // gqa_factor, D),
+            "caches must be [NB, 16, Hq/G, D]")
+    _expect(query.dtype == key_cache.dtype == value_cache.dtype, "query/cache dtype mismatch")
+    _expect(v_rows_read is None or (v_rows_read.dtype == torch.int64 and v_rows_read.numel() == 1),
+            "v_rows_read must be an int64 tensor of one element")
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.paged_attention_decode_splitkv_sparse_v(
+        _ptr(out), _dtype_code(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+        _dtype_code(key_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        B, Q, Hq, gqa_factor, D, key_cache.shape[1], key_cache.shape[0], float(scale),
+        float(v_threshold), _ptr(v_rows_read), int(max_context_len), int(partition_size),
         _ptr(workspace), nbytes, _stream(dev)))
 
 

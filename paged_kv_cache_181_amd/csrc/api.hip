@@ -437,6 +437,33 @@ int paged_attention_decode_cascade(void* out, int out_dtype, const void* query,
                        "paged_attention_decode_cascade");
 }
 
+int paged_attention_decode_splitkv_sparse_v(
+    void* out, int out_dtype, const void* query, const void* key_cache, const void* value_cache,
+    int kv_dtype, const int32_t* block_tables, int max_blocks_per_seq,
+    const int32_t* context_lens, int batch, int q_len, int num_q_heads, int gqa_factor,
+    int head_dim, int block_size, int64_t num_blocks, float scale, float v_threshold,
+    unsigned long long* v_rows_read, int max_context_len, int partition_size, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  if (kv_dtype != PKV_F16 && kv_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "kv_dtype must be PKV_F16 or PKV_BF16");
+  if (!(v_threshold >= 0.f && v_threshold < 1.f))
+    return fail(PKV_ERR_SHAPE, "v_threshold must be in [0, 1)");
+  pkv::AttnArgs a{};
+  int rc = check_attention(out, out_dtype, query, key_cache, value_cache, block_tables,
+                           max_blocks_per_seq, context_lens, batch, q_len, num_q_heads, gqa_factor,
+                           head_dim, block_size, num_blocks, scale, a);
+  if (rc) return rc;
+  if ((int64_t)gqa_factor * q_len > 4)
+    return fail(PKV_ERR_UNSUPPORTED, "sparse-V needs gqa_factor * q_len <= 4");
+  if (batch == 0) return ok();
+  rc = setup_split(a, head_dim, max_context_len, partition_size, workspace, workspace_bytes);
+  if (rc) return rc;
+  a.v_log2_threshold = v_threshold > 0.f ? std::log2(v_threshold) : -INFINITY;
+  a.v_rows_read = v_rows_read;
+  return launch_result(pkv::launch_sparse_v(a, kv_dtype, head_dim, (hipStream_t)stream),
+                       "paged_attention_decode_splitkv_sparse_v");
+}
+
 int paged_attention_decode_append(void* out, int out_dtype, const void* query,
                                   const void* new_key, const void* new_value, void* key_cache,
                                   void* value_cache, int kv_dtype, const int32_t* block_tables,

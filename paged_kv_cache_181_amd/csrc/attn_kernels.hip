@@ -691,6 +691,285 @@ void attn_partition_kernel(const AttnArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------------
+// Sparse-V partition kernel (approximate; 16-bit caches, G*q_len <= 4).
+//
+// The V row of position j is read only when some query row of the KV head has
+// weight 2^(s_j - m) >= threshold, m being that row's running maximum score so
+// far (log2 units, this block included).  A running maximum never exceeds the
+// final one, so every skipped row weighs less than `threshold` times the
+// row's largest weight; skipped positions still count in the softmax sum.
+// ("The KV Cache" (metalworking), arithmetic paragraph: sparse-V decode at 32K
+// is a KV-cache traffic deletion; the rule itself is this library's reading.)
+//
+// Rounds: each wavefront loads the K of up to 4 of its blocks at once (3 at
+// head_dim 128, for registers), scores them, and the workgroup's waves share
+// their row maxima through LDS, so the
+// reference maximum is the one over every block the partition has scored so
+// far (the whole partition when a round covers it).  Then the V rows some row
+// needs are requested for all of the round's blocks together (into the
+// registers the K rows used; the offsets of skipped rows are pushed out of the
+// buffer's range, so those lanes read zeros and touch no memory), and the PV
+// products follow.  V latency is exposed once per round, not once per block.
+constexpr uint32_t kOutOfRange = 0x7f000000u;   // past any block, no 32-bit wrap
+
+template <Fmt KV, int D>
+__global__ __launch_bounds__((8 * kWave), 4) void attn_sparse_v_kernel(const AttnArgs a) {
+  using MM = Mma<KV>;
+  using SM = AttnSmem<KV, D, 4>;
+  constexpr int NW = 8, RT = 4, GB = D == 128 ? 3 : 4;   // GB: blocks per wave per round
+  constexpr int KS = D / 32;
+  constexpr int NT = D / 16;
+  constexpr int QSTR = SM::QSTR;
+  static_assert(SM::NW == NW, "the 4-row 16-bit shape runs 8 wavefronts");
+  __shared__ __align__(16) unsigned char smem[SM::BYTES];
+  __shared__ __align__(16) uint16_t q_s[NW * RT * QSTR];
+  __shared__ float mm_s[NW][16], ml_s[NW][16];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rho = lane & 15, qd = lane >> 4;
+  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int Q = a.q_len, G = a.gqa, GQ = G * Q, Hq = a.num_q_heads;
+  const bool split = a.ws_o != nullptr;
+  const int64_t wsp = a.ws_parts;
+  const auto btr = span_rsrc(a.block_tables + (int64_t)b * a.max_blocks,
+                             (uint32_t)a.max_blocks * 4u);
+  const int bb = p * a.part_blocks;
+  int per = (a.part_blocks + NW - 1) / NW;
+  int tbl_next;
+  {
+    const int e = bb + w * per + lane;
+    tbl_next = lane < per ? buf_load<int>(btr, (uint32_t)e * 4u) : 0;
+  }
+  constexpr int QCW = RT * (D / 8);
+  u4 qv = u4{0u, 0u, 0u, 0u};
+  {
+    const int r = lane / (D / 8), c8 = lane % (D / 8);
+    if (lane < QCW && r < GQ)
+      qv = *(const u4*)((const uint16_t*)a.q +
+                        (((int64_t)b * Q + r / G) * Hq + g * G + r % G) * D + 8 * c8);
+  }
+  int L = a.context_lens[b];
+  L = min(max(L, 0), a.max_blocks * kBlock);
+  const int nblk = (L + kBlock - 1) / kBlock;
+  const int be = (p == a.num_parts - 1) ? nblk : min(nblk, bb + a.part_blocks);
+  if (split && bb >= be) {
+    for (int rr = threadIdx.x; rr < GQ; rr += NW * kWave) {
+      const int64_t pi = (((int64_t)b * Q + rr / G) * Hq + g * G + rr % G) * wsp + p;
+      a.ws_m[pi] = kNegInf;
+      a.ws_l[pi] = 0.f;
+    }
+    return;
+  }
+  if (be - bb > a.part_blocks) {
+    per = (be - bb + NW - 1) / NW;
+    const int e = bb + w * per + lane;
+    tbl_next = lane < per ? buf_load<int>(btr, (uint32_t)e * 4u) : 0;
+  }
+  const int w0 = bb + w * per;
+  const int nmine = max(0, min(per, be - w0));
+  const int rounds = (per + GB - 1) / GB;          // the same for every wave of the group
+  const bool row_ok = rho < GQ;
+  const int iq = row_ok ? rho / G : 0;
+  const int nvis = row_ok ? (L - Q + iq + 1) : L;
+  const int full_lim = L - Q + 1;
+
+  int tblv = tbl_next;
+  if (64 < per) {
+    const int kk = 64 + lane;
+    tbl_next = kk < nmine ? buf_load<int>(btr, (uint32_t)(w0 + kk) * 4u) : 0;
+  }
+  const LaneOffsets<KV, D> loff(a.num_kv_heads, g, rho, qd);
+  const uint32_t kblk = loff.kblk;
+  // K of run block j (zeros and no memory traffic past the run or for a table
+  // entry outside the pool); returns the mask of tokens with data
+  auto fetch_k = [&](int j, u4 (&kr)[KS]) -> uint32_t {
+    const int pb = __builtin_amdgcn_readlane(tblv, j & 63);
+    const bool ok = j < nmine && pb >= 0 && (int64_t)pb < a.num_blocks;
+    const auto kres = span_rsrc((const char*)a.k_cache + (int64_t)(ok ? pb : 0) * kblk,
+                                ok ? kblk : 0u);
+    const uint32_t ko = pin(loff.k);
+#pragma unroll
+    for (int m = 0; m < KS; ++m) kr[m] = buf_load<u4>(kres, ko + 64 * m);
+    const int left = L - (w0 + j) * kBlock;
+    return !ok ? 0u : left >= kBlock ? 0xffffu : (1u << max(left, 0)) - 1u;
+  };
+  // V of run block j for the tokens in `need` only
+  auto fetch_v = [&](int j, uint32_t need, u4 (&vr)[KS]) {
+    const int pb = __builtin_amdgcn_readlane(tblv, j & 63);
+    const bool ok = need != 0u && pb >= 0 && (int64_t)pb < a.num_blocks;
+    const auto vres = span_rsrc((const char*)a.v_cache + (int64_t)(ok ? pb : 0) * kblk,
+                                ok ? kblk : 0u);
+    const uint32_t vo = ((need >> rho) & 1u) ? pin(loff.v) : kOutOfRange;
+#pragma unroll
+    for (int m = 0; m < KS; ++m) vr[m] = buf_load<u4>(vres, vo + 64 * m);
+  };
+
+  uint16_t* qw = q_s + w * RT * QSTR;
+  if (lane < QCW) *(u4*)(qw + (lane / (D / 8)) * QSTR + 8 * (lane % (D / 8))) = qv;
+  wave_lds_fence();
+  const uint16_t* qrow = qw + (row_ok ? rho : rho % GQ) * QSTR;
+  unsigned char* vst = smem + w * (16 * D * 2);
+  const int tr_off = ((((rho & 3) >> 1) * 16) + 4 * qd + (rho >> 2)) * 16 + (rho & 1) * 8;
+
+  const float sl2 = a.scale_log2;
+  const float lt = a.v_log2_threshold;             // -inf: read every V row
+  float m_run = kNegInf, l_run = 0.f;
+  f4 o[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) o[n] = f4{0.f, 0.f, 0.f, 0.f};
+  uint32_t rows_read = 0;
+
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int k0 = rd * GB;
+    if (k0 > 0 && (k0 & 63) == 0) {                // next 64-entry chunk of the run
+      tblv = tbl_next;
+      const int kk = k0 + 64 + lane;
+      tbl_next = kk < nmine ? buf_load<int>(btr, (uint32_t)(w0 + kk) * 4u) : 0;
+    }
+    u4 buf[GB][KS];
+    uint32_t vm[GB];
+#pragma unroll
+    for (int u = 0; u < GB; ++u) vm[u] = fetch_k(k0 + u, buf[u]);
+    // scores of the round's blocks and this wave's row maximum over them
+    float sv[GB][4];
+    float mxw = kNegInf;
+#pragma unroll
+    for (int u = 0; u < GB; ++u) {
+      f4 s = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < KS; ++m) {
+        const u4 qm = *(const u4*)(qrow + 32 * m + 8 * qd);
+        s = MM::qk(buf[u][m], qm, s);
+      }
+      const int j0 = (w0 + k0 + u) * kBlock;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[u][r] = s[r] * sl2;
+      if (vm[u] != 0xffffu || j0 + kBlock > full_lim) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = j0 + 4 * qd + r;
+          if (!((vm[u] >> (4 * qd + r)) & 1u) || j >= nvis) sv[u][r] = kNegInf;
+        }
+      }
+      mxw = fmaxf(mxw, fmaxf(fmaxf(sv[u][0], sv[u][1]), fmaxf(sv[u][2], sv[u][3])));
+    }
+    mxw = quarter_max(mxw);
+    // the workgroup's row maximum over everything scored so far
+    if (qd == 0) mm_s[w][rho] = mxw;
+    __syncthreads();
+    float M = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, mm_s[ww][rho]);
+    __syncthreads();
+    if (M > m_run) {                                 // the reference moves up: rescale
+      const float alpha = m_run == kNegInf ? 0.f : fast_exp2(m_run - M);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) o[n] *= alpha;
+      l_run *= alpha;
+      m_run = M;
+    }
+    // the V rows some row of this head needs, for all of the round's blocks
+#pragma unroll
+    for (int u = 0; u < GB; ++u) {
+      uint32_t need = 0u;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool vote = row_ok && sv[u][r] != kNegInf && sv[u][r] >= m_run + lt;
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(vote);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if ((bal >> (16 * q)) & 0xffffull) need |= 1u << (4 * q + r);
+      }
+      rows_read += __builtin_popcount(need);
+      fetch_v(k0 + u, need, buf[u]);
+    }
+    // weights and PV, block by block
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+#pragma unroll
+    for (int u = 0; u < GB; ++u) {
+      float pr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sv[u][r] - m_use);
+      l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+#pragma unroll
+      for (int m = 0; m < KS; ++m) *(u4*)(vst + m * 1024 + lane * 16) = buf[u][m];
+      wave_lds_fence();
+      u2 phi, plo;
+      MM::split(pr, phi, plo);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const u2 av = lds_read_tr16(vst + tr_off + (n >> 1) * 1024 + (n & 1) * 512);
+        o[n] = MM::pv(av, phi, o[n]);
+        o[n] = MM::pv(av, plo, o[n]);
+      }
+      wave_lds_fence();
+    }
+  }
+  if (a.v_rows_read != nullptr && lane == 0)
+    atomicAdd((unsigned long long*)a.v_rows_read, (unsigned long long)rows_read);
+
+  l_run = quarter_sum(l_run);
+  __syncthreads();
+  float* mo = (float*)smem;
+  if (rho < RT && row_ok) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mo[(w * RT + rho) * D + 16 * n + 4 * qd + r] = o[n][r];
+  }
+  if (qd == 0) {
+    mm_s[w][rho] = m_run;
+    ml_s[w][rho] = l_run;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < GQ * D; idx += NW * kWave) {
+    const int rr = idx / D, d = idx % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, mm_s[ww][rr]);
+    const float Mu = M == kNegInf ? 0.f : M;
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float e = fast_exp2(mm_s[ww][rr] - Mu);
+      num += e * mo[(ww * RT + rr) * D + d];
+      den += e * ml_s[ww][rr];
+    }
+    const int64_t orow = ((int64_t)b * Q + rr / G) * Hq + g * G + rr % G;
+    if (split) {
+      const int64_t pi = orow * wsp + p;
+      a.ws_o[pi * D + d] = num;
+      if (d == 0) {
+        a.ws_m[pi] = M;
+        a.ws_l[pi] = den;
+      }
+    } else {
+      store_out(a.out, (OutT)a.out_dtype, orow * D + d, den > 0.f ? num / den : 0.f);
+    }
+  }
+}
+
+hipError_t launch_sparse_v(const AttnArgs& a, int kv_fmt, int head_dim, hipStream_t stream) {
+  if (a.batch == 0) return hipSuccess;
+  const dim3 grid((unsigned)a.num_parts, (unsigned)a.num_kv_heads, (unsigned)a.batch);
+  if (kv_fmt == (int)Fmt::F16) {
+    if (head_dim == 64)
+      hipLaunchKernelGGL((attn_sparse_v_kernel<Fmt::F16, 64>), grid, dim3(8 * kWave), 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_sparse_v_kernel<Fmt::F16, 128>), grid, dim3(8 * kWave), 0, stream, a);
+  } else {
+    if (head_dim == 64)
+      hipLaunchKernelGGL((attn_sparse_v_kernel<Fmt::BF16, 64>), grid, dim3(8 * kWave), 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_sparse_v_kernel<Fmt::BF16, 128>), grid, dim3(8 * kWave), 0, stream, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.ws_o == nullptr) return e;
+  return launch_attention(a, kv_fmt, kv_fmt, head_dim, stream, STAGE_MERGE);
+}
+
 // Log-sum-exp merge of the split-KV partials: one workgroup per output row
 // (b, i, h).  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, M = max_p m_p.
 // Single pass: thread (c, grp) takes partitions grp, grp+NG, ... for the 4

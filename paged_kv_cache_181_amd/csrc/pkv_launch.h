@@ -53,6 +53,8 @@ struct AttnArgs {
   const int32_t* grp_members;    // cascade: [num_groups, group_size] sequence ids (-1: empty)
   const int32_t* grp_prefix;     // cascade: [num_groups] shared whole blocks
   int num_groups, group_size;
+  float v_log2_threshold;        // sparse-V: skip V rows below 2^this of the running max
+  unsigned long long* v_rows_read;   // sparse-V: optional device counter of V rows read
 };
 
 // kv_fmt: 0 f16, 1 bf16, 3 k8v4; q_fmt: 0 f16, 1 bf16 (must equal kv_fmt unless k8v4).
@@ -61,5 +63,9 @@ struct AttnArgs {
 enum { STAGE_ALL = 0, STAGE_PARTIALS = 1, STAGE_MERGE = 2 };
 hipError_t launch_attention(const AttnArgs& a, int kv_fmt, int q_fmt, int head_dim,
                             hipStream_t stream, int stage = STAGE_ALL);
+
+// Sparse-V split-KV decode (16-bit caches, G*q_len <= 4): partition kernel
+// reading only the V rows some query row needs, then the merge.
+hipError_t launch_sparse_v(const AttnArgs& a, int kv_fmt, int head_dim, hipStream_t stream);
 
 }  // namespace pkv

@@ -769,3 +769,73 @@ def test_cascade_without_groups_is_plain_split(P):
     dc = DevCase(case)
     out = run_cascade(P, dc, np.zeros((0, 1), np.int32), np.zeros(0, np.int32), psize=32)
     assert max_err(out, ref) <= 2e-4
+
+
+# ------------------------------------------------------------------ sparse-V (approximate)
+
+def run_sparse(P, dc, tau, *, psize=512, q=None):
+    c = dc.case
+    q = dc.q if q is None else q
+    B, Q, Hq, D = q.shape
+    mcl = int(dc.cl.max().item())
+    n = P.splitkv_workspace_size(B, Q, Hq, D, mcl, psize)
+    ws = torch.full((max(n, 16) // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    rows = torch.zeros(1, dtype=torch.int64, device="cuda")
+    P.paged_attention_decode_splitkv_sparse_v(out, q, dc.k, dc.v, dc.bt, dc.cl, c.scale,
+                                              c.gqa_factor, tau, mcl, psize, ws, v_rows_read=rows)
+    torch.cuda.synchronize()
+    return out, int(rows.item())
+
+
+def visible_rows(case):
+    """(block, KV head, token) V rows with data: every position below the
+    length whose table entry names a pool block, once per KV head."""
+    total = 0
+    for b in range(case.batch):
+        L = min(int(case.context_lens[b]), case.max_blocks * 16)
+        for j in range(max(L, 0)):
+            blk = case.block_tables[b, j // 16]
+            total += 0 <= blk < case.num_blocks
+    return total * case.num_kv_heads
+
+
+@pytest.mark.parametrize("name", ["small_f16_d64", "small_bf16_d128_g4", "small_g1",
+                                  "llama8b_batch", "long32k"])
+def test_sparse_v_threshold_zero_is_exact(P, name):
+    case, ref = get_case(name)
+    dc = DevCase(case)
+    for psize in (512, 32):
+        out, rows = run_sparse(P, dc, 0.0, psize=psize)
+        assert max_err(out, ref) <= 2e-4
+        assert rows == visible_rows(case)
+
+
+def _peaked(case, factor=4.0):
+    """The same case with the queries multiplied by `factor` (exact in fp16:
+    a power of two), which sharpens every softmax row."""
+    import dataclasses
+    qf = oracle.decode(case.query, case.fmt) * factor
+    return dataclasses.replace(case, query=oracle.encode_f64(qf, case.fmt))
+
+
+@pytest.mark.parametrize("name,factor,tau", [
+    ("small_f16_d64", 1.0, 1e-3), ("small_bf16_d128_g4", 1.0, 1e-2),
+    ("llama8b_batch", 1.0, 1e-3), ("llama8b_batch", 4.0, 1e-4), ("llama8b_batch", 8.0, 1e-3),
+    ("long32k", 8.0, 1e-3), ("long32k", 8.0, 1e-4)])
+def test_sparse_v_stays_within_its_bound(P, name, factor, tau):
+    base, _ = get_case(name)
+    case = _peaked(base, factor) if factor != 1.0 else base
+    exact = oracle_decode(case)
+    bound = oracle.sparse_v_error_bound(case.query, case.key_cache, case.value_cache,
+                                        case.block_tables, case.context_lens, case.scale,
+                                        case.gqa_factor, case.fmt, tau)
+    dc = DevCase(case)
+    out, rows = run_sparse(P, dc, tau)
+    err = np.abs(out.cpu().numpy().astype(np.float64) - exact)
+    assert np.isfinite(err).all()
+    assert (err <= bound + 2e-4).all(), float((err - bound).max())
+    if factor > 1.0:                 # peaked rows: some V rows are never read ...
+        assert rows < visible_rows(case)
+    if factor >= 8.0 and tau >= 1e-3:  # ... and with sharp rows most of them
+        assert rows < 0.5 * visible_rows(case), rows / visible_rows(case)

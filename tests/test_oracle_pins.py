@@ -635,6 +635,31 @@ def test_planted_window_off_by_one_is_caught(monkeypatch):
     assert np.abs(run_oracle(case, window=8) - sdpa_reference(case, window=8)).max() > 1e-3
 
 
+def test_sparse_v_bound_is_zero_without_skipping_and_covers_a_brute_force_skip():
+    case = small_case(80, q_len=2, batch=3, lengths=[20, 45, 70])
+    assert not oracle.sparse_v_error_bound(case.query, case.key_cache, case.value_cache,
+                                           case.block_tables, case.context_lens, case.scale,
+                                           case.gqa_factor, case.fmt, 0.0).any()
+    # brute force on one row: drop every V below the threshold from the numerator
+    tau = 0.05
+    bound = oracle.sparse_v_error_bound(case.query, case.key_cache, case.value_cache,
+                                        case.block_tables, case.context_lens, case.scale,
+                                        case.gqa_factor, case.fmt, tau)
+    exact = run_oracle(case)
+    b, i, h = 2, 1, 5
+    L = int(case.context_lens[b])
+    K = contiguous_kv(case.key_cache, case.block_tables[b], L, case.fmt)
+    V = contiguous_kv(case.value_cache, case.block_tables[b], L, case.fmt)
+    n = L - case.q_len + i + 1
+    q = decode_bits(case.query[b, i, h], case.fmt)
+    s = float(np.float32(case.scale)) * (K[:n, h // case.gqa_factor] @ q)
+    w = np.exp(s - s.max())
+    keep = w >= tau
+    sparse = (w[keep, None] * V[:n, h // case.gqa_factor][keep]).sum(0) / w.sum()
+    err = np.abs(sparse - exact[b, i, h])
+    assert (err <= bound[b, i, h] + 1e-12).all() and bound[b, i, h].max() > 0
+
+
 def _sdpa_error(case):
     return np.abs(run_oracle(case) - sdpa_reference(case)).max()
 
