@@ -13,7 +13,12 @@
 //   G*q_len query rows that share a KV head live in one wavefront, so each K/V
 //   byte is read from HBM once.  The direct form is the same kernel with one
 //   partition per sequence; the split-KV form writes per-partition partials and
-//   a second kernel merges them by log-sum-exp.
+//   a second kernel merges them by log-sum-exp.  The same kernel also runs
+//   the append form (the new tokens stored and attended as one more tile), the
+//   sliding window (partitions counted from the window's first block) and the
+//   two cascade passes (a group's rows stacked in one tile over its shared
+//   prefix; each sequence past its group's prefix).  The approximate sparse-V
+//   kernel further down reads V rows selectively.
 //
 // Per 16-token block, per wavefront (lane l: row l % 16, quarter l / 16):
 //   - K rows are loaded straight into the A operand of a 16x16x32 MFMA
