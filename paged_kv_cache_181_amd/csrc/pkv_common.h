@@ -76,7 +76,6 @@ template <> struct Mma<Fmt::F16> {
     hi = u2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
     lo = u2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
   }
-  static __device__ __forceinline__ float to_f32(uint32_t bits16) { return f16_bits_to_f32(bits16); }
 };
 
 template <> struct Mma<Fmt::BF16> {
@@ -100,7 +99,6 @@ template <> struct Mma<Fmt::BF16> {
     hi = u2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
     lo = u2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
   }
-  static __device__ __forceinline__ float to_f32(uint32_t bits16) { return bf16_bits_to_f32(bits16); }
 };
 
 // ---------------------------------------------------------------- wave helpers
