@@ -33,6 +33,10 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python -m paged_kv_cache_181_amd.build` (hipcc, gfx950)")
+    # torch ships its own HIP runtime under the same soname; loading torch first
+    # makes the library bind to that one, so the process holds a single runtime
+    # (loaded the other way round, the library's calls find no device)
+    import torch  # noqa: F401
     return ctypes.CDLL(LIB_PATH)
 
 

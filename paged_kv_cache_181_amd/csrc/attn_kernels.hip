@@ -43,6 +43,18 @@
 // the per-token scale multiplies the scores; 4-bit V codes are converted exactly
 // and staged like 16-bit V, the per-group scale is folded into the weights
 // (sum_t p_t s_tg c_td) and the zero point into a per-group sum (sum_t p_t z_tg).
+// The conversions are bit tricks, a few instructions per 8 codes:
+//  - K: the offset-binary byte u = c + 128 becomes the fp16 1024 + u by placing
+//    it under the exponent byte 0x64 (one byte permute per two codes), or, for
+//    bf16 queries, the exact float of u truncated to bf16.  The constant offset
+//    (1152 or 128) times the row's query sum starts the score accumulator, so
+//    the scores come out exact (one MFMA pass per wave computes it).
+//  - V: each nibble, masked into an fp16 mantissa under 0x64, is 1024 + c; one
+//    packed fp16 subtract makes it c exactly.  The four mask shifts of a 32-bit
+//    word give the codes pairwise as (c0,c4), (c1,c5), (c2,c6), (c3,c7), and the
+//    V tile is staged in that order; the output dims are put back in order when
+//    the partial is written.  The PV products always run in fp16 (codes are
+//    small integers; the weights are split hi/lo).
 
 #include <math.h>
 
@@ -60,16 +72,50 @@ __device__ __forceinline__ int qk_dim(int m, int qd) {
   else return 32 * m + 8 * qd;
 }
 
-// int8 code -> 16-bit element bits of the MFMA type (exact: |c| <= 127).
-template <Fmt QT>
-__device__ __forceinline__ uint32_t code_bits(int c) {
-  if constexpr (QT == Fmt::F16) return f32_to_f16_bits((float)c);
-  else return __float_as_uint((float)c) >> 16;
-}
+// Four int8 K codes (one 32-bit word) -> two words of 16-bit MFMA elements
+// holding off + c exactly (off = kK8Offset), in dim order.
+template <Fmt QT> constexpr float kK8Offset = QT == Fmt::F16 ? 1152.f : 128.f;
+// -off in both halves of a word: the operand that makes off * sum(q)
+template <Fmt QT> constexpr uint32_t kK8NegOffset2 = QT == Fmt::F16 ? 0xE480E480u : 0xC300C300u;
 
 template <Fmt QT>
-__device__ __forceinline__ uint32_t pack2_codes(int c0, int c1) {
-  return code_bits<QT>(c0) | (code_bits<QT>(c1) << 16);
+__device__ __forceinline__ void k8_codes(uint32_t x, uint32_t& lo, uint32_t& hi) {
+  const uint32_t u = x ^ 0x80808080u;                    // bytes c + 128
+  if constexpr (QT == Fmt::F16) {
+    // {u.b0, 0x64, u.b1, 0x64}: fp16 (0x64 << 8 | u) = 1024 + u
+    lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+    hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+  } else {
+    // the float of an integer below 256 has 8 significant bits: its upper
+    // half is the exact bf16
+    const uint32_t f0 = __float_as_uint((float)(u & 0xffu));
+    const uint32_t f1 = __float_as_uint((float)((u >> 8) & 0xffu));
+    const uint32_t f2 = __float_as_uint((float)((u >> 16) & 0xffu));
+    const uint32_t f3 = __float_as_uint((float)(u >> 24));
+    lo = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
+    hi = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
+  }
+}
+
+// Eight 4-bit V codes (one 32-bit word, code k in bits 4k..4k+3) -> four words
+// of fp16 pairs (c0,c4), (c1,c5), (c2,c6), (c3,c7), exact.  A nibble in
+// mantissa bits 0..3 under exponent byte 0x64 is 1024 + c; in bits 4..7 under
+// 0x54 it is 64 + c (the unit in the last place there is 1/16).
+__device__ __forceinline__ u4 v4_codes(uint32_t w) {
+  const uint32_t w8 = w >> 8;
+  const h2 o1024 = h2{(_Float16)1024.f, (_Float16)1024.f}, o64 = h2{(_Float16)64.f, (_Float16)64.f};
+  const h2 v0 = __builtin_bit_cast(h2, (w & 0x000f000fu) | 0x64006400u) - o1024;
+  const h2 v1 = __builtin_bit_cast(h2, (w & 0x00f000f0u) | 0x54005400u) - o64;
+  const h2 v2 = __builtin_bit_cast(h2, (w8 & 0x000f000fu) | 0x64006400u) - o1024;
+  const h2 v3 = __builtin_bit_cast(h2, (w8 & 0x00f000f0u) | 0x54005400u) - o64;
+  return u4{__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1),
+            __builtin_bit_cast(uint32_t, v2), __builtin_bit_cast(uint32_t, v3)};
+}
+
+// Dim (within its 16-dim tile) of PV output row i of a staged K8/V4 tile:
+// position i & 7 of an 8-dim chunk holds dim ((i & 7) >> 1) + 4 * (i & 1).
+__device__ __forceinline__ constexpr int v4_dim(int i) {
+  return 8 * (i >> 3) + ((i & 7) >> 1) + 4 * (i & 1);
 }
 
 // Registers of one block for one lane.
@@ -424,6 +470,15 @@ void attn_partition_kernel(const AttnArgs a) {
   }
   wave_lds_fence();
   const uint16_t* qrow = qw + (row_ok ? rho : rho % GQ) * QSTR;   // this lane's operand row
+  // start of every score accumulator: 0, or for K8/V4 -off * (the row's query
+  // sum), which cancels the offset the converted K codes carry
+  f4 s_init = f4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (KV == Fmt::K8V4) {
+    constexpr uint32_t n2 = kK8NegOffset2<QT>;
+#pragma unroll
+    for (int m = 0; m < KS; ++m)
+      s_init = MM::qk(u4{n2, n2, n2, n2}, *(const u4*)(qrow + qk_dim<KV>(m, qd)), s_init);
+  }
 
   unsigned char* vst = smem + w * (16 * D * 2);             // this wave's staged V tile
   float* side = (float*)(smem + SM::VST) + w * 16 * (1 + 2 * GR);   // K8/V4 scales
@@ -451,22 +506,15 @@ void attn_partition_kernel(const AttnArgs a) {
     // ---- stage V in load-lane order: the 16-byte chunk (m, c) of token t at
     // m*1024 + (16c + t)*16, i.e. lane (t, c) of load m writes where it read.
     // Rows past the length are zeroed (their weight is 0, and 0 * NaN is NaN).
+    // K8/V4: the decoded codes are finite integers, so rows without data need
+    // no zeroing (their weights are exactly 0)
     if constexpr (KV == Fmt::K8V4) {
       constexpr int NC = D / 4;                 // codes held by this lane: dims NC*qd ..
       const uint32_t wd[4] = {br.v.x, br.v.y, br.v.z, br.v.w};
 #pragma unroll
       for (int q = 0; q < NC / 8; ++q) {        // 8 codes -> one 16-byte chunk
-        uint32_t pk[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t byte = (wd[q] >> (8 * e)) & 0xffu;
-          const int c0 = tok_ok ? (int)(byte & 0xfu) : 0;
-          const int c1 = tok_ok ? (int)(byte >> 4) : 0;
-          pk[e] = pack2_codes<QT>(c0, c1);
-        }
         const int dim0 = NC * qd + 8 * q;      // first dim of this chunk
-        *(u4*)(vst + (dim0 >> 5) * 1024 + (16 * ((dim0 & 31) >> 3) + rho) * 16) =
-            u4{pk[0], pk[1], pk[2], pk[3]};
+        *(u4*)(vst + (dim0 >> 5) * 1024 + (16 * ((dim0 & 31) >> 3) + rho) * 16) = v4_codes(wd[q]);
       }
     } else {
 #pragma unroll
@@ -478,7 +526,7 @@ void attn_partition_kernel(const AttnArgs a) {
     }
 
     // ---- scores S^T = K Q^T
-    f4 s = f4{0.f, 0.f, 0.f, 0.f};
+    f4 s = s_init;
     if constexpr (KV == Fmt::K8V4) {
 #pragma unroll
       for (int u = 0; u < D / 64; ++u) {
@@ -486,11 +534,7 @@ void attn_partition_kernel(const AttnArgs a) {
         const uint32_t wd[4] = {c.x, c.y, c.z, c.w};
         uint32_t cv[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int x = (int)wd[q];
-          cv[2 * q] = pack2_codes<QT>((int8_t)(x & 0xff), (int8_t)((x >> 8) & 0xff));
-          cv[2 * q + 1] = pack2_codes<QT>((int8_t)((x >> 16) & 0xff), (int8_t)((x >> 24) & 0xff));
-        }
+        for (int q = 0; q < 4; ++q) k8_codes<QT>(wd[q], cv[2 * q], cv[2 * q + 1]);
         const u4 q0 = *(const u4*)(qrow + qk_dim<KV>(2 * u, qd));
         const u4 q1 = *(const u4*)(qrow + qk_dim<KV>(2 * u + 1, qd));
         s = MM::qk(u4{cv[0], cv[1], cv[2], cv[3]}, q0, s);
@@ -499,7 +543,7 @@ void attn_partition_kernel(const AttnArgs a) {
       // per-token K scales and V scale/zero, moved through LDS from the
       // token-owner layout (lane rho) to the score layout (tokens 4*qd + r)
       if (qd == 0) {
-        side[rho] = f16_bits_to_f32(br.ks);
+        side[rho] = f16_bits_to_f32(br.ks) * sl2;
 #pragma unroll
         for (int gi = 0; gi < GR; ++gi) {
           const uint32_t sw = gi < 2 ? br.vs.x : br.vs.y;
@@ -523,7 +567,7 @@ void attn_partition_kernel(const AttnArgs a) {
     float sv[4];
     if constexpr (KV == Fmt::K8V4) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sv[r] = s[r] * side[4 * qd + r] * sl2;
+      for (int r = 0; r < 4; ++r) sv[r] = s[r] * side[4 * qd + r];
     } else {
 #pragma unroll
       for (int r = 0; r < 4; ++r) sv[r] = s[r] * sl2;
@@ -569,13 +613,13 @@ void attn_partition_kernel(const AttnArgs a) {
         }
         zacc[gi] += zs;
         u2 phi, plo;
-        MM::split(pw, phi, plo);
+        Mma<Fmt::F16>::split(pw, phi, plo);
 #pragma unroll
         for (int nn = 0; nn < 2; ++nn) {
           const int n = 2 * gi + nn;
           const u2 av = lds_read_tr16(vst + tr_off + (n >> 1) * 1024 + (n & 1) * 512);
-          o[n] = MM::pv(av, phi, o[n]);
-          o[n] = MM::pv(av, plo, o[n]);
+          o[n] = Mma<Fmt::F16>::pv(av, phi, o[n]);
+          o[n] = Mma<Fmt::F16>::pv(av, plo, o[n]);
         }
       }
     } else {
@@ -661,7 +705,10 @@ void attn_partition_kernel(const AttnArgs a) {
 #pragma unroll
     for (int n = 0; n < NT; ++n)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mo[(w * RT + rho) * D + 16 * n + 4 * qd + r] = o[n][r];
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * qd + r;              // output row within the tile
+        mo[(w * RT + rho) * D + 16 * n + (KV == Fmt::K8V4 ? v4_dim(i) : i)] = o[n][r];
+      }
   }
   if (qd == 0) {
     mm_s[w][rho] = m_run;

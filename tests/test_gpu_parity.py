@@ -839,3 +839,28 @@ def test_sparse_v_stays_within_its_bound(P, name, factor, tau):
         assert rows < visible_rows(case)
     if factor >= 8.0 and tau >= 1e-3:  # ... and with sharp rows most of them
         assert rows < 0.5 * visible_rows(case), rows / visible_rows(case)
+
+
+def test_library_loaded_before_torch_finds_the_device():
+    """Importing the binding before torch must still leave one HIP runtime in
+    the process (the binding loads torch first), so a call finds the GPU.  Runs
+    in a fresh interpreter, where nothing has imported torch yet."""
+    import os
+    import subprocess
+    import sys
+    code = ("import paged_kv_cache_181_amd._binding as B\n"
+            "import torch\n"
+            "import paged_kv_cache_181_amd as P\n"
+            "d = torch.device('cuda:0')\n"
+            "k = torch.randn(4, 2, 64, dtype=torch.float16, device=d)\n"
+            "v = torch.randn(4, 2, 64, dtype=torch.float16, device=d)\n"
+            "kc = torch.zeros(2, 16, 2, 64, dtype=torch.float16, device=d)\n"
+            "vc = torch.zeros_like(kc)\n"
+            "P.kv_cache_write(k, v, kc, vc, torch.tensor([0, 5, 17, 31], device=d))\n"
+            "torch.cuda.synchronize()\n"
+            "assert torch.equal(kc.view(32, 2, 64)[[0, 5, 17, 31]], k)\n"
+            "print('ok')\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                       timeout=110)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stderr[-2000:]
