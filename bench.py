@@ -298,7 +298,14 @@ def other_workload(name, P, W, torch, steps, warmup):
             pools.append(pool)
         per_tok_head = D + 2 + D // 2 + 4 * (D // 32)
 
-        def step():
+        def step():             # append form: quantize the new rows and attend, one call
+            for l in range(layers):
+                p = pools[l]
+                P.paged_attention_decode_splitkv_k8v4_append(
+                    out[l], q[l], nk[l], nv[l], p["k"], p["ks"], p["v"], p["vs"], p["vz"], bt, cl,
+                    scale, G, mcl, part, ws)
+
+        def step_two_call():    # the same step as quantize-on-write, then decode
             for l in range(layers):
                 p = pools[l]
                 P.kv_cache_write_k8v4(nk[l], nv[l], p["k"], p["ks"], p["v"], p["vs"], p["vz"], slots)
@@ -322,15 +329,19 @@ def other_workload(name, P, W, torch, steps, warmup):
                     P.paged_attention_decode_append(out[l], q[l], nk[l], nv[l], K[l], V[l], bt,
                                                     cl, scale, G)
     ms = time_steps(torch, graph_of(torch, step).replay, steps, warmup)
+    extra = {}
+    if name == "k8v4":
+        ms2 = time_steps(torch, graph_of(torch, step_two_call).replay, steps, warmup)
+        extra["two_call_us_per_layer"] = round(ms2 * 1e3 / layers, 3)
     layer_bytes = sum_len * Hkv * per_tok_head
     us = ms * 1e3 / layers
-    return {"us_per_layer": round(us, 3), "kv_bytes_per_layer": layer_bytes,
+    return {"us_per_layer": round(us, 3), **extra, "kv_bytes_per_layer": layer_bytes,
             "kv_stream_gbs": round(layer_bytes / (us * 1e-6) / 1e9, 2),
             "pct_of_hbm_peak": round(100 * layer_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
             "decode_rows_per_s": round(B * Q / (ms * 1e-3), 1),
             "layers": layers,
             "form": (f"split-KV partition {part}" if part else "direct")
-            + (", quantize-on-write + decode" if name == "k8v4"
+            + (", append form (quantize-on-write in the decode launch)" if name == "k8v4"
                else f", write + sliding window {window}" if window else ", append form")
             + ", HIP graph",
             "writes_per_layer": T, "kv_format": "k8v4" if name == "k8v4" else fmt}

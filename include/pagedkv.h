@@ -414,6 +414,40 @@ int paged_attention_decode_splitkv_k8v4_partials(
     void* stream);
 
 /*
+ * paged_attention_decode_k8v4_append / paged_attention_decode_splitkv_k8v4_append —
+ * the K8/V4 decode step with the quantize-on-write folded into the attention
+ * launch (mlxcel "KV Cache", Attention Dispatch and In-Place Decode Writes; the
+ * quantization is that of kv_cache_write_k8v4).  The result, in `out` and in
+ * the five cache arrays, is that of
+ *     kv_cache_write_k8v4(new_key, new_value, q_dtype, k_cache, ..., slots, ...)
+ * followed by paged_attention_decode[_splitkv]_k8v4(...) with the same
+ * arguments, the slots being those the block tables give the new positions
+ * (as for paged_attention_decode_append): codes and scales bit-exact, the
+ * attention over the quantized new rows.
+ *   new_key, new_value: [batch * q_len, num_kv_heads, head_dim] of q_dtype
+ *   k_cache, k_scale, v_cache, v_scale, v_zero: written (the new rows) and read
+ * New tokens whose position is negative or whose table entry lies outside
+ * [0, num_blocks) are neither stored nor attended.  Every other argument, the
+ * workspace and the errors are those of the unfused calls.
+ */
+int paged_attention_decode_k8v4_append(void* out, int out_dtype, const void* query, int q_dtype,
+                                       const void* new_key, const void* new_value,
+                                       int8_t* k_cache, void* k_scale, uint8_t* v_cache,
+                                       void* v_scale, void* v_zero, const int32_t* block_tables,
+                                       int max_blocks_per_seq, const int32_t* context_lens,
+                                       int batch, int q_len, int num_q_heads, int gqa_factor,
+                                       int head_dim, int block_size, int64_t num_blocks,
+                                       float scale, void* stream);
+
+int paged_attention_decode_splitkv_k8v4_append(
+    void* out, int out_dtype, const void* query, int q_dtype, const void* new_key,
+    const void* new_value, int8_t* k_cache, void* k_scale, uint8_t* v_cache, void* v_scale,
+    void* v_zero, const int32_t* block_tables, int max_blocks_per_seq,
+    const int32_t* context_lens, int batch, int q_len, int num_q_heads, int gqa_factor,
+    int head_dim, int block_size, int64_t num_blocks, float scale, int max_context_len,
+    int partition_size, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Cache bytes one token occupies over all layers (host-only arithmetic).
  * "The KV Cache", arithmetic paragraph: one K and one V vector per KV head per
  * layer; fp16/bf16: 2 * layers * kv_heads * head_dim * 2.  K8/V4:

@@ -61,6 +61,9 @@ SIGNATURES = {
     "kv_cache_write_k8v4": ([_p, _p, _i, _p, _p, _p, _p, _p, _p, _i64, _i, _i, _i, _i64, _p], _i),
     "paged_attention_decode_k8v4": (_ATTN_K8V4 + [_p], _i),
     "paged_attention_decode_splitkv_k8v4": (_ATTN_K8V4 + [_i, _i, _p, _sz, _p], _i),
+    "paged_attention_decode_k8v4_append": (_ATTN_K8V4[:4] + [_p, _p] + _ATTN_K8V4[4:] + [_p], _i),
+    "paged_attention_decode_splitkv_k8v4_append": (
+        _ATTN_K8V4[:4] + [_p, _p] + _ATTN_K8V4[4:] + [_i, _i, _p, _sz, _p], _i),
     "kv_cache_bytes_per_token": ([_i, _i, _i, _i, ctypes.POINTER(_i64)], _i),
     "paged_attention_decode_splitkv_partials": (_ATTN[2:] + [_i, _i, _p, _sz, _p], _i),
     "paged_attention_decode_splitkv_k8v4_partials": (_ATTN_K8V4[2:] + [_i, _i, _p, _sz, _p], _i),
@@ -444,6 +447,50 @@ def paged_attention_decode_splitkv_k8v4(out, query, k_cache, k_scale, v_cache, v
         _ptr(v_cache), _ptr(v_scale), _ptr(v_zero), _ptr(block_tables), block_tables.shape[1],
         _ptr(context_lens), B, Q, Hq, gqa_factor, D, bs, nb, float(scale), int(max_context_len),
         int(partition_size), _ptr(workspace), nbytes, _stream(dev)))
+
+
+def _k8v4_append_check(query, new_key, new_value, k_cache):
+    B, Q, Hq, D = query.shape
+    hkv = k_cache.shape[2]
+    for t in (new_key, new_value):
+        _expect(t.shape == (B * Q, hkv, D) and t.dtype == query.dtype and t.is_contiguous(),
+                "new_key / new_value must be [batch * q_len, Hkv, D] of the query dtype")
+
+
+def paged_attention_decode_k8v4_append(out, query, new_key, new_value, k_cache, k_scale, v_cache,
+                                       v_scale, v_zero, block_tables, context_lens, scale,
+                                       gqa_factor):
+    """Quantize-on-write of the new rows and K8/V4 decode, one launch."""
+    dev = _dev(out, query, new_key, new_value, k_cache, k_scale, v_cache, v_scale, v_zero,
+               block_tables, context_lens)
+    B, Q, Hq, D = _attn_common(out, query, block_tables, context_lens, gqa_factor)
+    nb, bs = _k8v4_check(query, gqa_factor, k_cache, k_scale, v_cache, v_scale, v_zero)
+    _k8v4_append_check(query, new_key, new_value, k_cache)
+    _check(lib.paged_attention_decode_k8v4_append(
+        _ptr(out), _dtype_code(out), _ptr(query), _dtype_code(query), _ptr(new_key),
+        _ptr(new_value), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache), _ptr(v_scale), _ptr(v_zero),
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, Q, Hq, gqa_factor, D,
+        bs, nb, float(scale), _stream(dev)))
+
+
+def paged_attention_decode_splitkv_k8v4_append(out, query, new_key, new_value, k_cache, k_scale,
+                                               v_cache, v_scale, v_zero, block_tables,
+                                               context_lens, scale, gqa_factor, max_context_len,
+                                               partition_size, workspace):
+    """Quantize-on-write of the new rows and split-KV K8/V4 decode (partition
+    kernel, then the merge)."""
+    dev = _dev(out, query, new_key, new_value, k_cache, k_scale, v_cache, v_scale, v_zero,
+               block_tables, context_lens, workspace)
+    B, Q, Hq, D = _attn_common(out, query, block_tables, context_lens, gqa_factor)
+    nb, bs = _k8v4_check(query, gqa_factor, k_cache, k_scale, v_cache, v_scale, v_zero)
+    _k8v4_append_check(query, new_key, new_value, k_cache)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.paged_attention_decode_splitkv_k8v4_append(
+        _ptr(out), _dtype_code(out), _ptr(query), _dtype_code(query), _ptr(new_key),
+        _ptr(new_value), _ptr(k_cache), _ptr(k_scale), _ptr(v_cache), _ptr(v_scale), _ptr(v_zero),
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, Q, Hq, gqa_factor, D,
+        bs, nb, float(scale), int(max_context_len), int(partition_size), _ptr(workspace), nbytes,
+        _stream(dev)))
 
 
 def paged_attention_decode_splitkv_partials(query, key_cache, value_cache, block_tables,

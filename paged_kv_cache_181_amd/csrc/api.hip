@@ -569,6 +569,69 @@ int paged_attention_decode_splitkv_k8v4(void* out, int out_dtype, const void* qu
                        "paged_attention_decode_splitkv_k8v4");
 }
 
+int paged_attention_decode_k8v4_append(void* out, int out_dtype, const void* query, int q_dtype,
+                                       const void* new_key, const void* new_value,
+                                       int8_t* k_cache, void* k_scale, uint8_t* v_cache,
+                                       void* v_scale, void* v_zero, const int32_t* block_tables,
+                                       int max_blocks_per_seq, const int32_t* context_lens,
+                                       int batch, int q_len, int num_q_heads, int gqa_factor,
+                                       int head_dim, int block_size, int64_t num_blocks,
+                                       float scale, void* stream) {
+  if (q_dtype != PKV_F16 && q_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "q_dtype must be PKV_F16 or PKV_BF16");
+  pkv::AttnArgs a{};
+  int rc = check_attention(out, out_dtype, query, k_cache, v_cache, block_tables,
+                           max_blocks_per_seq, context_lens, batch, q_len, num_q_heads, gqa_factor,
+                           head_dim, block_size, num_blocks, scale, a);
+  if (rc) return rc;
+  if (batch == 0) return ok();
+  rc = check_k8v4_pointers(k_scale, v_scale, v_zero);
+  if (rc) return rc;
+  if (!new_key || !new_value) return fail(PKV_ERR_NULL, "new_key / new_value is NULL");
+  if (!aligned16(new_key) || !aligned16(new_value))
+    return fail(PKV_ERR_ALIGN, "new_key and new_value must be 16-byte aligned");
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.v_zero = v_zero;
+  a.new_k = new_key;
+  a.new_v = new_value;
+  return launch_result(pkv::launch_attention(a, PKV_FMT_K8V4, q_dtype, head_dim,
+                                             (hipStream_t)stream),
+                       "paged_attention_decode_k8v4_append");
+}
+
+int paged_attention_decode_splitkv_k8v4_append(
+    void* out, int out_dtype, const void* query, int q_dtype, const void* new_key,
+    const void* new_value, int8_t* k_cache, void* k_scale, uint8_t* v_cache, void* v_scale,
+    void* v_zero, const int32_t* block_tables, int max_blocks_per_seq,
+    const int32_t* context_lens, int batch, int q_len, int num_q_heads, int gqa_factor,
+    int head_dim, int block_size, int64_t num_blocks, float scale, int max_context_len,
+    int partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+  if (q_dtype != PKV_F16 && q_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "q_dtype must be PKV_F16 or PKV_BF16");
+  pkv::AttnArgs a{};
+  int rc = check_attention(out, out_dtype, query, k_cache, v_cache, block_tables,
+                           max_blocks_per_seq, context_lens, batch, q_len, num_q_heads, gqa_factor,
+                           head_dim, block_size, num_blocks, scale, a);
+  if (rc) return rc;
+  if (batch == 0) return ok();
+  rc = check_k8v4_pointers(k_scale, v_scale, v_zero);
+  if (rc) return rc;
+  if (!new_key || !new_value) return fail(PKV_ERR_NULL, "new_key / new_value is NULL");
+  if (!aligned16(new_key) || !aligned16(new_value))
+    return fail(PKV_ERR_ALIGN, "new_key and new_value must be 16-byte aligned");
+  rc = setup_split(a, head_dim, max_context_len, partition_size, workspace, workspace_bytes);
+  if (rc) return rc;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.v_zero = v_zero;
+  a.new_k = new_key;
+  a.new_v = new_value;
+  return launch_result(pkv::launch_attention(a, PKV_FMT_K8V4, q_dtype, head_dim,
+                                             (hipStream_t)stream),
+                       "paged_attention_decode_splitkv_k8v4_append");
+}
+
 int paged_attention_decode_splitkv_partials(const void* query, const void* key_cache,
                                             const void* value_cache, int kv_dtype,
                                             const int32_t* block_tables, int max_blocks_per_seq,

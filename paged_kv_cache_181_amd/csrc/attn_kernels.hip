@@ -57,6 +57,7 @@
 //    small integers; the weights are split hi/lo).
 
 #include <math.h>
+#include <stddef.h>
 
 #include "pkv_common.h"
 #include "pkv_launch.h"
@@ -228,12 +229,13 @@ __device__ __forceinline__ void load_block(const AttnArgs& a, int64_t pb, bool l
 }
 
 // Workgroup shape: RT query rows per KV head tile (4 when G*q_len <= 4, else
-// 16).  The 16-bit 4-row form runs 8 wavefronts at 4 per SIMD (128 registers);
-// the K8/V4 and 16-row forms, which hold more per lane, 4 wavefronts at 3.
+// 16).  The 16-bit 4-row form runs 8 wavefronts at 4 per SIMD (128 registers),
+// the K8/V4 4-row form 4 wavefronts at 4 per SIMD, and the 16-row forms,
+// which hold more per lane, 4 wavefronts at 3.
 template <Fmt KV, int RT> struct Shape {
   static constexpr bool WIDE = RT == 4 && KV != Fmt::K8V4;
   static constexpr int NW = WIDE ? 8 : 4;
-  static constexpr int WAVES_PER_SIMD = WIDE ? 4 : 3;
+  static constexpr int WAVES_PER_SIMD = RT == 4 ? 4 : 3;
 };
 
 template <Fmt KV, int D, int RT>
@@ -246,6 +248,10 @@ struct AttnSmem {
   static constexpr int MO = NW * RT * D * 4;               // merge: per-wave outputs
   static constexpr int LOOP = VST + SIDE;
   static constexpr int BYTES = LOOP > MO ? LOOP : MO;
+  // append form: the new tokens' tile, parked from the start of the launch to
+  // the end of the block loop (lanes of rows rho < RT), after the loop area
+  static constexpr int STASH = RT * 4 * (int)sizeof(BlockRegs<KV, D>);
+  static constexpr int BYTES_APPEND = LOOP + STASH > MO ? LOOP + STASH : MO;
   static constexpr int QSTR = D + 8;                       // halves per staged query row
 };
 
@@ -288,7 +294,7 @@ void attn_partition_kernel(const AttnArgs a) {
   constexpr int NT = D / 16;           // PV output tiles
   constexpr int GR = SM::GR;
   constexpr int QSTR = SM::QSTR;
-  __shared__ __align__(16) unsigned char smem[SM::BYTES];
+  __shared__ __align__(16) unsigned char smem[SM::BYTES_APPEND];
   __shared__ __align__(16) uint16_t q_s[NW * RT * QSTR];
   __shared__ float mm_s[NW][16], ml_s[NW][16];
 
@@ -354,7 +360,7 @@ void attn_partition_kernel(const AttnArgs a) {
   // Append form: the q_len new tokens (positions L-Q .. L-1) come from the
   // new K/V rows, not the cache; the partition holding position L-1 attends
   // to them and stores them into the cache.  Cache blocks then cover Lc.
-  const bool append = KV != Fmt::K8V4 && a.new_k != nullptr;
+  const bool append = a.new_k != nullptr;
   const int Lc = append ? max(L - Q, 0) : L;                // positions read from the cache
   const int nblk = (Lc + kBlock - 1) / kBlock;
   // Sliding window W: row i (position L-Q+i) sees positions L-Q+i-W+1 ..
@@ -458,8 +464,149 @@ void attn_partition_kernel(const AttnArgs a) {
     if (lo0 > jb) m &= ~((1u << min(lo0 - jb, kBlock)) - 1u);   // before every window
     return ok ? m : 0u;
   };
+  // ---- append form, first half: the last wave of the partition holding
+  // position L-1 takes the new tokens (token t at position L-Q+t, rows past
+  // q_len read as zeros).  Their rows are requested before the first block's,
+  // stored into their cache slots (K8/V4: quantized first, exactly as the
+  // quantize-on-write does) while the block loads are in flight, and parked
+  // in LDS as one more tile for the end of the block loop.
+  const bool app_wave = append && p == p_new && w == NW - 1;          // wave-uniform
+  u4 nkh[D / 32], nvh[D / 32];        // 16-bit: this lane's new-row halves, 8 per u4
+  uint32_t nkw[RT], nvw[RT];          // K8/V4: token t's halves of dims lane*E .. +E-1
+  constexpr int E = D / kWave;        // K8/V4 quantization: dims per lane and token
+  if (app_wave) {
+    const uint32_t rows_b = (uint32_t)(Q * a.num_kv_heads * D * 2);
+    const int64_t first = (int64_t)b * Q * a.num_kv_heads * D * 2;
+    const auto kr = span_rsrc((const char*)a.new_k + first, rows_b);
+    const auto vr = span_rsrc((const char*)a.new_v + first, rows_b);
+    const uint32_t row0 = (uint32_t)((rho * a.num_kv_heads + g) * D * 2);
+    if constexpr (KV == Fmt::K8V4) {
+      // quantized a token at a time with the wave spread over its dims (as the
+      // quantize-on-write does), rows t >= q_len read as zeros
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const uint32_t off = (uint32_t)(((t * a.num_kv_heads + g) * D + lane * E) * 2);
+        if constexpr (E == 2) {
+          nkw[t] = buf_load<uint32_t>(kr, off);
+          nvw[t] = buf_load<uint32_t>(vr, off);
+        } else {
+          nkw[t] = buf_load<uint16_t>(kr, off);
+          nvw[t] = buf_load<uint16_t>(vr, off);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m) nkh[m] = buf_load<u4>(kr, loff.k + 64 * m);
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m) nvh[m] = buf_load<u4>(vr, loff.v + 64 * m);
+    }
+  }
   BlockRegs<KV, D> r0, r1;
   uint32_t ok0 = fetch(0, 0, min(64, nmine), r0), ok1 = 0u;
+  unsigned char* stash = smem + SM::LOOP;
+  const bool tv = tnew >= 0 && (int64_t)tnew < a.num_blocks;   // rho < Q, position >= 0
+  if (app_wave) {
+    if constexpr (KV != Fmt::K8V4) {
+      BlockRegs<KV, D> rn;
+      const int pos = L - Q + rho;
+      const int64_t row = ((int64_t)tnew * kBlock + (pos & (kBlock - 1))) * a.num_kv_heads + g;
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m) {
+        rn.k[m] = nkh[m];
+        rn.v[m] = nvh[m];
+      }
+      if (tv) {
+        char* kd = (char*)a.k_cache + row * (D * 2) + 16 * qd;
+        char* vd = (char*)a.v_cache + row * (D * 2) + 16 * qd;
+#pragma unroll
+        for (int m = 0; m < D / 32; ++m) {
+          *(u4*)(kd + 64 * m) = rn.k[m];
+          *(u4*)(vd + 64 * m) = rn.v[m];
+        }
+      }
+      if (rho < RT) *(BlockRegs<KV, D>*)(stash + (qd * RT + rho) * sizeof(BlockRegs<KV, D>)) = rn;
+    } else {
+      // Token by token, lane l quantizing dims l*E .. +E-1 exactly as the
+      // quantize-on-write does; the codes and scales go to the cache and into
+      // the parked tile, whose lane (token rho, quarter qd) layout is that of
+      // a loaded block (K dims 64u + 16qd .. +15, V dims (D/4)qd .. +D/4-1).
+      using BR = BlockRegs<KV, D>;
+      constexpr int SZ = (int)sizeof(BR), GL = 32 / E;       // GL: lanes per V group
+      constexpr int OK_ = (int)offsetof(BR, k), OV = (int)offsetof(BR, v);
+      constexpr int OKS = (int)offsetof(BR, ks), OVS = (int)offsetof(BR, vs), OVZ = (int)offsetof(BR, vz);
+#pragma unroll
+      for (int i = lane; i < RT * 4 * SZ / 16; i += kWave) *(u4*)(stash + 16 * i) = u4{0u, 0u, 0u, 0u};
+      wave_lds_fence();
+      const int d0 = lane * E;
+      auto to_f = [&](uint32_t h) -> float {
+        return QT == Fmt::F16 ? f16_bits_to_f32(h & 0xffffu) : bf16_bits_to_f32(h & 0xffffu);
+      };
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        if (t >= Q) break;                                   // wave-uniform
+        float k[E], v[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          k[e] = to_f(nkw[t] >> (16 * e));
+          v[e] = to_f(nvw[t] >> (16 * e));
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(k[e]));
+#pragma unroll
+        for (int m = 1; m < kWave; m <<= 1) amax = fmaxf(amax, wave_xor(amax, m));
+        const uint16_t ks16 = k8_scale_bits(amax);
+        const float ks = f16_bits_to_f32(ks16), rks = __builtin_amdgcn_rcpf(ks);
+        uint32_t kc = 0u;                                    // E codes, little-endian
+#pragma unroll
+        for (int e = 0; e < E; ++e) kc |= (uint32_t)(k8_code(k[e], ks, rks) & 0xff) << (8 * e);
+        float mn = v[0], mx = v[0];
+#pragma unroll
+        for (int e = 1; e < E; ++e) { mn = fminf(mn, v[e]); mx = fmaxf(mx, v[e]); }
+#pragma unroll
+        for (int m = 1; m < GL; m <<= 1) {
+          mn = fminf(mn, wave_xor(mn, m));
+          mx = fmaxf(mx, wave_xor(mx, m));
+        }
+        const uint16_t vs16 = v4_scale_bits(mn, mx), vz16 = f32_to_f16_bits(mn);
+        const float vs = f16_bits_to_f32(vs16), vz = f16_bits_to_f32(vz16);
+        const float rvs = __builtin_amdgcn_rcpf(vs);
+        uint32_t vb = v4_code(v[0], vs, rvs, vz);            // this lane's V byte (E == 2) ...
+        if constexpr (E == 2) vb |= v4_code(v[1], vs, rvs, vz) << 4;
+        else vb |= (uint32_t)__shfl_down((int)vb, 1, kWave) << 4;   // ... or even lanes' (E == 1)
+        const bool vlead = E == 2 || (lane & 1) == 0;
+        const int gi = d0 / 32;                              // this lane's V group
+        // cache slot of token t (its table entry is lane t's)
+        const int tn = __builtin_amdgcn_readlane(tnew, t);
+        if (tn >= 0 && (int64_t)tn < a.num_blocks) {
+          const int64_t row = ((int64_t)tn * kBlock + ((L - Q + t) & (kBlock - 1))) * a.num_kv_heads + g;
+          char* kd = (char*)a.k_cache + row * D + d0;
+          if constexpr (E == 2) *(uint16_t*)kd = (uint16_t)kc;
+          else *(uint8_t*)kd = (uint8_t)kc;
+          if (vlead) ((uint8_t*)a.v_cache)[row * (D / 2) + d0 / 2] = (uint8_t)vb;
+          if (lane == 0) ((uint16_t*)a.k_scale)[row] = ks16;
+          if (lane % GL == 0) {
+            ((uint16_t*)a.v_scale)[row * GR + gi] = vs16;
+            ((uint16_t*)a.v_zero)[row * GR + gi] = vz16;
+          }
+        }
+        // the parked tile
+        unsigned char* ek = stash + (((d0 % 64) / 16) * RT + t) * SZ + OK_ + 16 * (d0 / 64) + d0 % 16;
+        if constexpr (E == 2) *(uint16_t*)ek = (uint16_t)kc;
+        else *ek = (uint8_t)kc;
+        constexpr int NV = D / 4;                            // V dims per quarter
+        if (vlead) stash[((d0 / NV) * RT + t) * SZ + OV + (d0 % NV) / 2] = (uint8_t)vb;
+        if (lane < 4) *(uint16_t*)(stash + (lane * RT + t) * SZ + OKS) = ks16;
+        if (lane % GL == 0) {
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            *(uint16_t*)(stash + (q4 * RT + t) * SZ + OVS + 2 * gi) = vs16;
+            *(uint16_t*)(stash + (q4 * RT + t) * SZ + OVZ + 2 * gi) = vz16;
+          }
+        }
+      }
+    }
+  }
 
   // ---- stage the query rows in this wave's own LDS area
   uint16_t* qw = q_s + w * RT * QSTR;
@@ -658,35 +805,12 @@ void attn_partition_kernel(const AttnArgs a) {
     }
   }
 
-  // ---- append form: the last wave of the partition holding position L-1
-  // takes the new tokens as one more tile (token t at position L-Q+t, rows
-  // past q_len read as zeros) and stores them into their cache slots.
-  if constexpr (KV != Fmt::K8V4) {
-    if (p == p_new && w == NW - 1) {
-      BlockRegs<KV, D> rn;
-      const uint32_t rows_b = (uint32_t)(Q * a.num_kv_heads * D * 2);
-      const int64_t first = (int64_t)b * Q * a.num_kv_heads * D * 2;
-      const auto kr = span_rsrc((const char*)a.new_k + first, rows_b);
-      const auto vr = span_rsrc((const char*)a.new_v + first, rows_b);
-#pragma unroll
-      for (int m = 0; m < D / 32; ++m) rn.k[m] = buf_load<u4>(kr, loff.k + 64 * m);
-#pragma unroll
-      for (int m = 0; m < D / 32; ++m) rn.v[m] = buf_load<u4>(vr, loff.v + 64 * m);
-      const bool tv = tnew >= 0 && (int64_t)tnew < a.num_blocks;   // rho < Q, position >= 0
-      const uint32_t vmask = (uint32_t)__builtin_amdgcn_ballot_w64(tv && qd == 0) & 0xffffu;
-      if (tv) {
-        const int pos = L - Q + rho;
-        const int64_t row = ((int64_t)tnew * kBlock + (pos & (kBlock - 1))) * a.num_kv_heads + g;
-        char* kd = (char*)a.k_cache + row * (D * 2) + 16 * qd;
-        char* vd = (char*)a.v_cache + row * (D * 2) + 16 * qd;
-#pragma unroll
-        for (int m = 0; m < D / 32; ++m) {
-          *(u4*)(kd + 64 * m) = rn.k[m];
-          *(u4*)(vd + 64 * m) = rn.v[m];
-        }
-      }
-      process(L - Q, vmask, rn);
-    }
+  // ---- append form, second half: the parked tile of new tokens
+  if (app_wave) {
+    BlockRegs<KV, D> rn{};
+    if (rho < RT) rn = *(const BlockRegs<KV, D>*)(stash + (qd * RT + rho) * sizeof(BlockRegs<KV, D>));
+    const uint32_t vmask = (uint32_t)__builtin_amdgcn_ballot_w64(tv && qd == 0) & 0xffffu;
+    process(L - Q, vmask, rn);
   }
 
   // ---- per-wave totals: the sum is spread over the four quarters

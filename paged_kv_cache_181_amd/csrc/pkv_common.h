@@ -44,6 +44,47 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t bits16) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
 
+// ---------------------------------------------------------------- K8/V4 quantization
+//
+// The arithmetic of the quantize-on-write, in one place for every kernel that
+// stores K8/V4 rows ("How MTPLX Manages Memory Using Request-Sized Paged KV
+// Cache", Quantization-Aware Memory Layout; the formulas are this library's
+// reading): K per (token, head) symmetric int8 with an fp16 scale, V per group
+// of 32 dims asymmetric 4-bit with fp16 scale and zero.  fp32 throughout, the
+// divisions correctly rounded, ties of the rounding to even.
+
+// fp16 bits of the K scale of a row whose largest magnitude is amax
+__device__ __forceinline__ uint16_t k8_scale_bits(float amax) {
+  return f32_to_f16_bits(__fdiv_rn(amax, 127.0f));
+}
+// rint(fdiv_rn(x, s)) (ties to even), with rs = the hardware reciprocal of s.
+// x * rs is within 1.5 units in the last place of x / s, far below 2^-13 for
+// the quotients met here (|x / s| < 300), so when it lies farther than 2^-13
+// from a half-integer it rounds to the same integer as the correctly rounded
+// quotient; otherwise the exact division decides.
+__device__ __forceinline__ float rint_div(float x, float s, float rs) {
+  const float q = x * rs;
+  float c = rintf(q);
+  if (fabsf(q - c) > 0.5f - 0x1p-13f) c = rintf(__fdiv_rn(x, s));
+  return c;
+}
+// the code of k under the (fp16-exact) scale s (rs: its reciprocal, as above)
+__device__ __forceinline__ int k8_code(float k, float s, float rs) {
+  float c = 0.f;
+  if (s != 0.f) c = fminf(fmaxf(rint_div(k, s, rs), -127.f), 127.f);
+  return (int)c;
+}
+// fp16 bits of the V scale of a group spanning [mn, mx] (the zero is fp16(mn))
+__device__ __forceinline__ uint16_t v4_scale_bits(float mn, float mx) {
+  return f32_to_f16_bits(__fdiv_rn(mx - mn, 15.0f));
+}
+// the code of v under the (fp16-exact) scale s and zero z
+__device__ __forceinline__ uint32_t v4_code(float v, float s, float rs, float z) {
+  float c = 0.f;
+  if (s != 0.f) c = fminf(fmaxf(rint_div(v - z, s, rs), 0.f), 15.f);
+  return (uint32_t)c;
+}
+
 // ---------------------------------------------------------------- MFMA wrappers
 //
 // S^T = K . Q^T uses the 16x16x32 form (K tile rows = 16 tokens, reduction over

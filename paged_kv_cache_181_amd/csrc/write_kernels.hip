@@ -83,16 +83,12 @@ __global__ __launch_bounds__(256) void kv_write_k8v4_kernel(
   for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(k[e]));
 #pragma unroll
   for (int m = 1; m < kWave; m <<= 1) amax = fmaxf(amax, wave_xor(amax, m));
-  const float ks32 = __fdiv_rn(amax, 127.0f);
-  const uint16_t ks16 = f32_to_f16_bits(ks32);
+  const uint16_t ks16 = k8_scale_bits(amax);
   const float ks = f16_bits_to_f32(ks16);
   const int64_t dst_row = slot * hkv + h;            // (block, row, head) flattened
+  const float rks = __builtin_amdgcn_rcpf(ks);
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    float c = 0.f;
-    if (ks != 0.f) c = fminf(fmaxf(rintf(__fdiv_rn(k[e], ks)), -127.f), 127.f);
-    k_cache[dst_row * D + lane * E + e] = (int8_t)(int)c;
-  }
+  for (int e = 0; e < E; ++e) k_cache[dst_row * D + lane * E + e] = (int8_t)k8_code(k[e], ks, rks);
   if (lane == 0) k_scale[dst_row] = ks16;
 
   // ---- V: asymmetric 4-bit per group of 32 (32 / E lanes per group)
@@ -105,16 +101,13 @@ __global__ __launch_bounds__(256) void kv_write_k8v4_kernel(
     mn = fminf(mn, wave_xor(mn, m));
     mx = fmaxf(mx, wave_xor(mx, m));
   }
-  const uint16_t vs16 = f32_to_f16_bits(__fdiv_rn(mx - mn, 15.0f));
+  const uint16_t vs16 = v4_scale_bits(mn, mx);
   const uint16_t vz16 = f32_to_f16_bits(mn);
   const float vs = f16_bits_to_f32(vs16), vz = f16_bits_to_f32(vz16);
   uint32_t code[E];
+  const float rvs = __builtin_amdgcn_rcpf(vs);
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    float c = 0.f;
-    if (vs != 0.f) c = fminf(fmaxf(rintf(__fdiv_rn(v[e] - vz, vs)), 0.f), 15.f);
-    code[e] = (uint32_t)c;
-  }
+  for (int e = 0; e < E; ++e) code[e] = v4_code(v[e], vs, rvs, vz);
   if constexpr (E == 2) {
     v_cache[dst_row * (D / 2) + lane] = (uint8_t)(code[0] | (code[1] << 4));
   } else {

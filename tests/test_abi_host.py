@@ -177,7 +177,7 @@ def test_append_argument_errors(P):
     bad[4] = ctypes.c_void_p(4104)
     assert lib.paged_attention_decode_append(*bad, None) == -6
     bad = list(base)
-    bad[7] = 3                                        # no K8/V4 append form
+    bad[7] = 3                                        # K8/V4 has its own append calls
     assert lib.paged_attention_decode_append(*bad, None) == -3
     assert lib.paged_attention_decode_splitkv_append(*base, 64, 512, None, 0, None) == -4
     assert lib.paged_attention_decode_splitkv_append(*base, 64, 40, FAKE, 1 << 30, None) == -3
@@ -186,6 +186,39 @@ def test_append_argument_errors(P):
     for i in (0, 2, 3, 4, 5, 6, 8, 10):
         zero[i] = None
     assert lib.paged_attention_decode_append(*zero, None) == 0
+
+
+def test_k8v4_append_argument_errors(P):
+    lib = P.lib
+    # out, out_dtype, query, q_dtype, new_key, new_value, k, ks, v, vs, vz, bt, mb, cl,
+    # B, Q, Hq, G, D, bs, nb, scale
+    base = [FAKE, 0, FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE,
+            2, 1, 32, 4, 128, 16, 64, 0.1]
+    for fn in (lib.paged_attention_decode_k8v4_append,
+               lambda *a: lib.paged_attention_decode_splitkv_k8v4_append(
+                   *a[:-1], 64, 512, FAKE, 1 << 30, None)):
+        bad = list(base)
+        bad[4] = None
+        assert fn(*bad, None) == -1
+        bad = list(base)
+        bad[5] = ctypes.c_void_p(4104)
+        assert fn(*bad, None) == -6
+        bad = list(base)
+        bad[3] = 2                                    # queries and new rows are f16 or bf16
+        assert fn(*bad, None) == -3
+        bad = list(base)
+        bad[7] = None
+        assert fn(*bad, None) == -1
+        bad = list(base)
+        bad[18] = 96
+        assert fn(*bad, None) == -3
+        zero = list(base)
+        zero[14] = 0
+        for i in (0, 2, 4, 5, 6, 7, 8, 9, 10, 11, 13):
+            zero[i] = None
+        assert fn(*zero, None) == 0
+    assert lib.paged_attention_decode_splitkv_k8v4_append(*base, 64, 512, None, 0, None) == -4
+    assert lib.paged_attention_decode_splitkv_k8v4_append(*base, 64, 40, FAKE, 1 << 30, None) == -3
 
 
 def test_gather_argument_errors(P):
