@@ -102,13 +102,22 @@ __device__ __forceinline__ void k8_codes(uint32_t x, uint32_t& lo, uint32_t& hi)
 // of fp16 pairs (c0,c4), (c1,c5), (c2,c6), (c3,c7), exact.  A nibble in
 // mantissa bits 0..3 under exponent byte 0x64 is 1024 + c; in bits 4..7 under
 // 0x54 it is 64 + c (the unit in the last place there is 1/16).
-__device__ __forceinline__ u4 v4_codes(uint32_t w) {
+// The mask and magic constants live in registers (masks in scalar, magics in
+// vector registers: one scalar operand per instruction), which lets each
+// mask-and-insert be one v_and_or_b32.
+struct V4Consts {
+  uint32_t m0 = 0x000f000fu, m1 = 0x00f000f0u, e0 = 0x64006400u, e1 = 0x54005400u;
+  __device__ __forceinline__ V4Consts() {
+    asm volatile("" : "+s"(m0), "+s"(m1), "+v"(e0), "+v"(e1));
+  }
+};
+__device__ __forceinline__ u4 v4_codes(uint32_t w, const V4Consts& c) {
   const uint32_t w8 = w >> 8;
   const h2 o1024 = h2{(_Float16)1024.f, (_Float16)1024.f}, o64 = h2{(_Float16)64.f, (_Float16)64.f};
-  const h2 v0 = __builtin_bit_cast(h2, (w & 0x000f000fu) | 0x64006400u) - o1024;
-  const h2 v1 = __builtin_bit_cast(h2, (w & 0x00f000f0u) | 0x54005400u) - o64;
-  const h2 v2 = __builtin_bit_cast(h2, (w8 & 0x000f000fu) | 0x64006400u) - o1024;
-  const h2 v3 = __builtin_bit_cast(h2, (w8 & 0x00f000f0u) | 0x54005400u) - o64;
+  const h2 v0 = __builtin_bit_cast(h2, (w & c.m0) | c.e0) - o1024;
+  const h2 v1 = __builtin_bit_cast(h2, (w & c.m1) | c.e1) - o64;
+  const h2 v2 = __builtin_bit_cast(h2, (w8 & c.m0) | c.e0) - o1024;
+  const h2 v3 = __builtin_bit_cast(h2, (w8 & c.m1) | c.e1) - o64;
   return u4{__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1),
             __builtin_bit_cast(uint32_t, v2), __builtin_bit_cast(uint32_t, v3)};
 }
@@ -642,6 +651,7 @@ void attn_partition_kernel(const AttnArgs a) {
   for (int gi = 0; gi < GR; ++gi) zacc[gi] = 0.f;
 
   const float sl2 = a.scale_log2;
+  const V4Consts v4c;                   // (used by K8/V4 only)
 
   // One tile of 16 tokens at positions j0 .. j0+15; bit t of vmask says
   // whether token t holds data (wave-uniform).
@@ -661,7 +671,7 @@ void attn_partition_kernel(const AttnArgs a) {
 #pragma unroll
       for (int q = 0; q < NC / 8; ++q) {        // 8 codes -> one 16-byte chunk
         const int dim0 = NC * qd + 8 * q;      // first dim of this chunk
-        *(u4*)(vst + (dim0 >> 5) * 1024 + (16 * ((dim0 & 31) >> 3) + rho) * 16) = v4_codes(wd[q]);
+        *(u4*)(vst + (dim0 >> 5) * 1024 + (16 * ((dim0 & 31) >> 3) + rho) * 16) = v4_codes(wd[q], v4c);
       }
     } else {
 #pragma unroll

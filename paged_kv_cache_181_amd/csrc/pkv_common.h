@@ -104,18 +104,16 @@ template <> struct Mma<Fmt::F16> {
     return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4, a),
                                                  __builtin_bit_cast(h4, b), c, 0, 0, 0);
   }
-  // p -> (hi, lo) with hi = f16(p), lo = f16(p - hi): hi + lo carries ~22 bits of p.
+  // p -> (hi, lo): hi = f16 of p rounded toward zero (one packed conversion
+  // per pair), lo = f16_rne(p - hi), written straight into its half; the
+  // difference is exact in fp32, so hi + lo carries ~21 bits of p.
   static __device__ __forceinline__ void split(const float p[4], u2& hi, u2& lo) {
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      _Float16 ph = (_Float16)p[r];
-      _Float16 pl = (_Float16)(p[r] - (float)ph);
-      h[r] = __builtin_bit_cast(uint16_t, ph);
-      l[r] = __builtin_bit_cast(uint16_t, pl);
-    }
-    hi = u2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-    lo = u2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+    const h2 h01 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(p[0], p[1]));
+    const h2 h23 = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(p[2], p[3]));
+    const h2 l01 = h2{(_Float16)(p[0] - (float)h01.x), (_Float16)(p[1] - (float)h01.y)};
+    const h2 l23 = h2{(_Float16)(p[2] - (float)h23.x), (_Float16)(p[3] - (float)h23.y)};
+    hi = u2{__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
+    lo = u2{__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)};
   }
 };
 
