@@ -383,6 +383,9 @@ int kv_cache_write_k8v4(const void* key, const void* value, int in_dtype, int8_t
  * paged_attention_decode_k8v4 — paged_attention_decode over the K8/V4 arrays
  * above, dequantizing in registers (k = code * s; v = code * s + z).
  * query and out as in paged_attention_decode with query of q_dtype (f16/bf16).
+ * Range: the V scales enter fp16 products as weight * scale with weights up
+ * to 2^8, so every V scale must stay below 65504 / 2^8 (a V group spanning
+ * less than about 3800); beyond that the output is not finite.
  */
 int paged_attention_decode_k8v4(void* out, int out_dtype, const void* query, int q_dtype,
                                 const int8_t* k_cache, const void* k_scale,
