@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (scale for rocprofv3 byte counters)")
+    ap.add_argument("--only", default=None,
+                    help="time only this one of the other workloads (for profiling), e.g. k8v4")
     return ap.parse_args()
 
 
@@ -512,6 +514,21 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.only:
+        runners = {n: (lambda n=n: other_workload(n, P, W, torch, args.steps, args.warmup))
+                   for n in OTHER}
+        runners["cascade_system_prompt"] = lambda: cascade_workload(P, W, torch, args.steps,
+                                                                    args.warmup)
+        runners["sparse_v_long32k_peaked"] = lambda: sparse_v_workload(P, W, torch, args.steps,
+                                                                       args.warmup)
+        runners["gather_llama8b_batch"] = lambda: gather_workload(P, W, torch, args.steps,
+                                                                  args.warmup)
+        if args.only not in runners:
+            print(json.dumps({"error": f"unknown workload {args.only}; one of {sorted(runners)}"}))
+            sys.exit(2)
+        log(f"timing {args.only}")
+        print(json.dumps({"workload": args.only, **runners[args.only]()}), flush=True)
         return
 
     log("building the 32K workload")

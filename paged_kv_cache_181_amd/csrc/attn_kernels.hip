@@ -479,7 +479,16 @@ void attn_partition_kernel(const AttnArgs a) {
   // stored into their cache slots (K8/V4: quantized first, exactly as the
   // quantize-on-write does) while the block loads are in flight, and parked
   // in LDS as one more tile for the end of the block loop.
-  const bool app_wave = append && p == p_new && w == NW - 1;          // wave-uniform
+  // When the new tokens share the sequence's last cache block (that block
+  // then holds cache rows too: always so for one new token unless it starts a
+  // block), they are patched into that block's registers by the wave that
+  // owns it, and no extra tile is needed; otherwise the partition's last wave
+  // attends to them as one extra tile after its blocks.
+  const int blk_new = (L - 1) / kBlock;                     // the block of position L-1
+  const int new_row0 = (L - Q) & (kBlock - 1);              // the first new token's row
+  const bool patch = append && L - Q > 0 && new_row0 != 0 && (L - Q) / kBlock == blk_new;
+  const bool app_wave = append && p == p_new &&
+                        w == (patch ? (blk_new - b0) / max(per, 1) : NW - 1);   // wave-uniform
   u4 nkh[D / 32], nvh[D / 32];        // 16-bit: this lane's new-row halves, 8 per u4
   uint32_t nkw[RT], nvw[RT];          // K8/V4: token t's halves of dims lane*E .. +E-1
   constexpr int E = D / kWave;        // K8/V4 quantization: dims per lane and token
@@ -656,6 +665,12 @@ void attn_partition_kernel(const AttnArgs a) {
   // One tile of 16 tokens at positions j0 .. j0+15; bit t of vmask says
   // whether token t holds data (wave-uniform).
   auto process = [&](int j0, uint32_t vmask, BlockRegs<KV, D>& br) {
+    if (app_wave && patch && j0 == blk_new * kBlock) {       // wave-uniform, once
+      // the parked new rows replace the block's rows new_row0 .. new_row0+Q-1
+      const int t = rho - new_row0;
+      if (t >= 0 && t < Q) br = *(const BlockRegs<KV, D>*)(stash + (qd * RT + t) * sizeof(BlockRegs<KV, D>));
+      vmask |= ((uint32_t)__builtin_amdgcn_ballot_w64(tv && qd == 0) & ((1u << Q) - 1u)) << new_row0;
+    }
     const bool tail = vmask != 0xffffu;                      // some tokens hold no data
     const bool full = !tail && j0 >= lo_max && j0 + kBlock <= full_lim;   // no masking at all
     const bool tok_ok = (vmask >> rho) & 1u;                 // this lane's token (rho) exists
@@ -816,7 +831,7 @@ void attn_partition_kernel(const AttnArgs a) {
   }
 
   // ---- append form, second half: the parked tile of new tokens
-  if (app_wave) {
+  if (app_wave && !patch) {
     BlockRegs<KV, D> rn{};
     if (rho < RT) rn = *(const BlockRegs<KV, D>*)(stash + (qd * RT + rho) * sizeof(BlockRegs<KV, D>));
     const uint32_t vmask = (uint32_t)__builtin_amdgcn_ballot_w64(tv && qd == 0) & 0xffffu;
