@@ -318,12 +318,18 @@ def other_workload(name, P, W, torch, steps, warmup):
         V = [rnd(NB, 16, Hkv, D) for _ in range(layers)]
         per_tok_head = 4 * D
 
+        def step_two_call():    # the windowed step as write, then windowed split-KV decode
+            for l in range(layers):
+                P.kv_cache_write(nk[l], nv[l], K[l], V[l], slots)
+                P.paged_attention_decode_splitkv_window(out[l], q[l], K[l], V[l], bt, cl, scale,
+                                                        G, window, mcl, part, ws)
+
         def step():             # append form: store the new rows and attend, one call
             for l in range(layers):
-                if window:      # the windowed step: write, then windowed split-KV decode
-                    P.kv_cache_write(nk[l], nv[l], K[l], V[l], slots)
-                    P.paged_attention_decode_splitkv_window(out[l], q[l], K[l], V[l], bt, cl,
-                                                            scale, G, window, mcl, part, ws)
+                if window:
+                    P.paged_attention_decode_splitkv_window_append(out[l], q[l], nk[l], nv[l],
+                                                                   K[l], V[l], bt, cl, scale, G,
+                                                                   window, mcl, part, ws)
                 elif part:
                     P.paged_attention_decode_splitkv_append(out[l], q[l], nk[l], nv[l], K[l], V[l],
                                                             bt, cl, scale, G, mcl, part, ws)
@@ -332,7 +338,7 @@ def other_workload(name, P, W, torch, steps, warmup):
                                                     cl, scale, G)
     ms = time_steps(torch, graph_of(torch, step).replay, steps, warmup)
     extra = {}
-    if name == "k8v4":
+    if name == "k8v4" or window:
         ms2 = time_steps(torch, graph_of(torch, step_two_call).replay, steps, warmup)
         extra["two_call_us_per_layer"] = round(ms2 * 1e3 / layers, 3)
     layer_bytes = sum_len * Hkv * per_tok_head
@@ -344,7 +350,7 @@ def other_workload(name, P, W, torch, steps, warmup):
             "layers": layers,
             "form": (f"split-KV partition {part}" if part else "direct")
             + (", append form (quantize-on-write in the decode launch)" if name == "k8v4"
-               else f", write + sliding window {window}" if window else ", append form")
+               else f", append form, sliding window {window}" if window else ", append form")
             + ", HIP graph",
             "writes_per_layer": T, "kv_format": "k8v4" if name == "k8v4" else fmt}
 

@@ -244,6 +244,33 @@ int paged_attention_decode_splitkv_window(void* out, int out_dtype, const void* 
                                           size_t workspace_bytes, void* stream);
 
 /*
+ * paged_attention_decode_window_append / paged_attention_decode_splitkv_window_append —
+ * the windowed decode step with the slot write folded into the attention
+ * launch: the result, in `out` and in the caches, is that of
+ * paged_attention_decode_append's write followed by
+ * paged_attention_decode[_splitkv]_window with the same arguments (the new
+ * rows are stored whether or not any window reaches them).  Arguments,
+ * workspace (sized for the window's span S) and errors as for those calls.
+ * 16-bit caches only.
+ */
+int paged_attention_decode_window_append(void* out, int out_dtype, const void* query,
+                                         const void* new_key, const void* new_value,
+                                         void* key_cache, void* value_cache, int kv_dtype,
+                                         const int32_t* block_tables, int max_blocks_per_seq,
+                                         const int32_t* context_lens, int batch, int q_len,
+                                         int num_q_heads, int gqa_factor, int head_dim,
+                                         int block_size, int64_t num_blocks, float scale,
+                                         int sliding_window, void* stream);
+
+int paged_attention_decode_splitkv_window_append(
+    void* out, int out_dtype, const void* query, const void* new_key, const void* new_value,
+    void* key_cache, void* value_cache, int kv_dtype, const int32_t* block_tables,
+    int max_blocks_per_seq, const int32_t* context_lens, int batch, int q_len, int num_q_heads,
+    int gqa_factor, int head_dim, int block_size, int64_t num_blocks, float scale,
+    int sliding_window, int max_context_len, int partition_size, void* workspace,
+    size_t workspace_bytes, void* stream);
+
+/*
  * paged_attention_decode_cascade — split-KV decode for batches whose
  * sequences share whole-block prefixes in groups (mlxcel "KV Cache", Paged
  * Decode Storage and Kernels: cascade attention for groups that share a

@@ -22,7 +22,8 @@ _EXPORTS = (
     "paged_attention_decode_window", "paged_attention_decode_splitkv_window", "gather_kv_cache",
     "paged_attention_decode_cascade", "cascade_workspace_size",
     "paged_attention_decode_splitkv_sparse_v", "paged_attention_decode_k8v4_append",
-    "paged_attention_decode_splitkv_k8v4_append",
+    "paged_attention_decode_splitkv_k8v4_append", "paged_attention_decode_window_append",
+    "paged_attention_decode_splitkv_window_append",
 )
 
 __all__ = list(_EXPORTS)

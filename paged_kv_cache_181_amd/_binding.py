@@ -80,6 +80,9 @@ SIGNATURES = {
     "paged_attention_decode_cascade": (_ATTN + [_p, _p, _i, _i, _i, _i, _i, _p, _sz, _p], _i),
     "paged_attention_decode_splitkv_sparse_v": (_ATTN + [_f, _p, _i, _i, _p, _sz, _p], _i),
     "paged_attention_decode_splitkv_window": (_ATTN + [_i, _i, _i, _p, _sz, _p], _i),
+    "paged_attention_decode_window_append": (_ATTN[:3] + [_p, _p] + _ATTN[3:] + [_i, _p], _i),
+    "paged_attention_decode_splitkv_window_append": (_ATTN[:3] + [_p, _p] + _ATTN[3:]
+                                                     + [_i, _i, _i, _p, _sz, _p], _i),
 }
 for _name, (_args, _res) in SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -323,6 +326,34 @@ def paged_attention_decode_splitkv_window(out, query, key_cache, value_cache, bl
         B, Q, Hq, gqa_factor, D, key_cache.shape[1], key_cache.shape[0], float(scale),
         int(sliding_window), int(max_context_len), int(partition_size), _ptr(workspace), nbytes,
         _stream(dev)))
+
+
+def paged_attention_decode_window_append(out, query, new_key, new_value, key_cache, value_cache,
+                                         block_tables, context_lens, scale, gqa_factor,
+                                         sliding_window):
+    """Slot write of the new rows and direct decode over each row's
+    ``sliding_window`` most recent positions, in one launch."""
+    dev = _dev(out, query, new_key, new_value, key_cache, value_cache, block_tables, context_lens)
+    args = _append_args(out, query, new_key, new_value, key_cache, value_cache, block_tables,
+                        context_lens, gqa_factor)
+    _check(lib.paged_attention_decode_window_append(*args, float(scale), int(sliding_window),
+                                                    _stream(dev)))
+
+
+def paged_attention_decode_splitkv_window_append(out, query, new_key, new_value, key_cache,
+                                                 value_cache, block_tables, context_lens, scale,
+                                                 gqa_factor, sliding_window, max_context_len,
+                                                 partition_size, workspace):
+    """Slot write of the new rows and windowed split-KV decode (partition
+    kernel, then the merge)."""
+    dev = _dev(out, query, new_key, new_value, key_cache, value_cache, block_tables, context_lens,
+               workspace)
+    args = _append_args(out, query, new_key, new_value, key_cache, value_cache, block_tables,
+                        context_lens, gqa_factor)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.paged_attention_decode_splitkv_window_append(
+        *args, float(scale), int(sliding_window), int(max_context_len), int(partition_size),
+        _ptr(workspace), nbytes, _stream(dev)))
 
 
 def gather_kv_cache(key_cache, value_cache, block_tables, cu_seq_lens, max_seq_len, key_out,

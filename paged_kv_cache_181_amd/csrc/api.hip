@@ -346,6 +346,64 @@ int paged_attention_decode_splitkv_window(void* out, int out_dtype, const void* 
                        "paged_attention_decode_splitkv_window");
 }
 
+int paged_attention_decode_window_append(void* out, int out_dtype, const void* query,
+                                         const void* new_key, const void* new_value,
+                                         void* key_cache, void* value_cache, int kv_dtype,
+                                         const int32_t* block_tables, int max_blocks_per_seq,
+                                         const int32_t* context_lens, int batch, int q_len,
+                                         int num_q_heads, int gqa_factor, int head_dim,
+                                         int block_size, int64_t num_blocks, float scale,
+                                         int sliding_window, void* stream) {
+  if (kv_dtype != PKV_F16 && kv_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "kv_dtype must be PKV_F16 or PKV_BF16");
+  if (sliding_window < 0) return fail(PKV_ERR_SHAPE, "sliding_window must be >= 0");
+  pkv::AttnArgs a{};
+  int rc = check_attention(out, out_dtype, query, key_cache, value_cache, block_tables,
+                           max_blocks_per_seq, context_lens, batch, q_len, num_q_heads, gqa_factor,
+                           head_dim, block_size, num_blocks, scale, a);
+  if (rc) return rc;
+  if (batch == 0) return ok();
+  if (!new_key || !new_value) return fail(PKV_ERR_NULL, "new_key / new_value is NULL");
+  if (!aligned16(new_key) || !aligned16(new_value))
+    return fail(PKV_ERR_ALIGN, "new_key and new_value must be 16-byte aligned");
+  a.window = sliding_window;
+  a.new_k = new_key;
+  a.new_v = new_value;
+  return launch_result(pkv::launch_attention(a, kv_dtype, kv_dtype, head_dim, (hipStream_t)stream),
+                       "paged_attention_decode_window_append");
+}
+
+int paged_attention_decode_splitkv_window_append(
+    void* out, int out_dtype, const void* query, const void* new_key, const void* new_value,
+    void* key_cache, void* value_cache, int kv_dtype, const int32_t* block_tables,
+    int max_blocks_per_seq, const int32_t* context_lens, int batch, int q_len, int num_q_heads,
+    int gqa_factor, int head_dim, int block_size, int64_t num_blocks, float scale,
+    int sliding_window, int max_context_len, int partition_size, void* workspace,
+    size_t workspace_bytes, void* stream) {
+  if (kv_dtype != PKV_F16 && kv_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "kv_dtype must be PKV_F16 or PKV_BF16");
+  if (sliding_window < 0) return fail(PKV_ERR_SHAPE, "sliding_window must be >= 0");
+  pkv::AttnArgs a{};
+  int rc = check_attention(out, out_dtype, query, key_cache, value_cache, block_tables,
+                           max_blocks_per_seq, context_lens, batch, q_len, num_q_heads, gqa_factor,
+                           head_dim, block_size, num_blocks, scale, a);
+  if (rc) return rc;
+  if (batch == 0) return ok();
+  if (!new_key || !new_value) return fail(PKV_ERR_NULL, "new_key / new_value is NULL");
+  if (!aligned16(new_key) || !aligned16(new_value))
+    return fail(PKV_ERR_ALIGN, "new_key and new_value must be 16-byte aligned");
+  const int span = sliding_window > 0
+                       ? (int)std::min<int64_t>(max_context_len, (int64_t)sliding_window + q_len + 15)
+                       : max_context_len;
+  rc = setup_split(a, head_dim, span, partition_size, workspace, workspace_bytes);
+  if (rc) return rc;
+  a.window = sliding_window;
+  a.new_k = new_key;
+  a.new_v = new_value;
+  return launch_result(pkv::launch_attention(a, kv_dtype, kv_dtype, head_dim, (hipStream_t)stream),
+                       "paged_attention_decode_splitkv_window_append");
+}
+
 int paged_attention_decode_cascade_workspace_size(int batch, int q_len, int num_q_heads,
                                                   int head_dim, int max_context_len,
                                                   int max_prefix_len, int partition_size,

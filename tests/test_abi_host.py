@@ -188,6 +188,36 @@ def test_append_argument_errors(P):
     assert lib.paged_attention_decode_append(*zero, None) == 0
 
 
+def test_window_append_argument_errors(P):
+    lib = P.lib
+    # out, out_dtype, query, new_key, new_value, k, v, kv_dtype, bt, mb, cl, B, Q, Hq, G, D, bs,
+    # nb, scale, window
+    base = [FAKE, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 4, FAKE, 2, 1, 32, 4, 128, 16, 64, 0.1, 64]
+    for fn in (lib.paged_attention_decode_window_append,
+               lambda *a: lib.paged_attention_decode_splitkv_window_append(
+                   *a[:-1], 64, 512, FAKE, 1 << 30, None)):
+        bad = list(base)
+        bad[3] = None
+        assert fn(*bad, None) == -1
+        bad = list(base)
+        bad[4] = ctypes.c_void_p(4104)
+        assert fn(*bad, None) == -6
+        bad = list(base)
+        bad[7] = 3                                    # 16-bit caches only
+        assert fn(*bad, None) == -3
+        bad = list(base)
+        bad[19] = -1
+        assert fn(*bad, None) == -2
+        zero = list(base)
+        zero[11] = 0
+        for i in (0, 2, 3, 4, 5, 6, 8, 10):
+            zero[i] = None
+        assert fn(*zero, None) == 0
+    assert lib.paged_attention_decode_splitkv_window_append(*base, 64, 512, None, 0, None) == -4
+    assert lib.paged_attention_decode_splitkv_window_append(*base, 64, 40, FAKE, 1 << 30,
+                                                            None) == -3
+
+
 def test_k8v4_append_argument_errors(P):
     lib = P.lib
     # out, out_dtype, query, q_dtype, new_key, new_value, k, ks, v, vs, vz, bt, mb, cl,

@@ -727,6 +727,77 @@ def test_window_matches_oracle(P, name, window, split, psize):
     assert err <= 2e-4, f"{name} W={window}: fp32-out max abs err {err}"
 
 
+WINDOW_APPEND_CASES = [
+    ("small_f16_d64", 1), ("small_f16_d64", 17), ("small_bf16_d128_g4", 33),
+    ("small_verify_q4", 5), ("small_g8_q2", 7), ("edge_lengths", 2), ("edge_lengths", 16),
+    ("long32k", 2048),
+]
+_window_append_refs = {}
+
+
+def window_append_ref(name, window):
+    """The oracle's step: store the new rows at their table slots, then the
+    windowed decode over the updated caches."""
+    if (name, window) not in _window_append_refs:
+        case, _ = get_case(name)
+        slots = oracle.append_slots(case.block_tables, case.context_lens, case.q_len,
+                                    case.num_blocks)
+        kc, vc = oracle.kv_cache_write(case.new_key, case.new_value, case.key_cache,
+                                       case.value_cache, slots)
+        ref = oracle.paged_attention(case.query, kc, vc, case.block_tables, case.context_lens,
+                                     case.scale, case.gqa_factor, case.fmt, window=window)
+        _window_append_refs[(name, window)] = (ref, kc, vc)
+    return _window_append_refs[(name, window)]
+
+
+def run_window_append(P, dc, window, *, split, psize=512, out_dtype=torch.float32):
+    c = dc.case
+    k, v = dc.k.clone(), dc.v.clone()
+    out = torch.full(dc.q.shape, float("nan"), dtype=out_dtype, device="cuda")
+    if split:
+        mcl = int(dc.cl.max().item())
+        B, Q, Hq, D = dc.q.shape
+        span = min(mcl, window + Q + 15) if window else mcl
+        n = P.splitkv_workspace_size(B, Q, Hq, D, span, psize)
+        ws = torch.full((max(n, 16) // 4 + 4,), float("nan"), dtype=torch.float32, device="cuda")
+        P.paged_attention_decode_splitkv_window_append(out, dc.q, dc.new_k, dc.new_v, k, v, dc.bt,
+                                                       dc.cl, c.scale, c.gqa_factor, window, mcl,
+                                                       psize, ws)
+    else:
+        P.paged_attention_decode_window_append(out, dc.q, dc.new_k, dc.new_v, k, v, dc.bt, dc.cl,
+                                               c.scale, c.gqa_factor, window)
+    torch.cuda.synchronize()
+    return out, k, v
+
+
+@pytest.mark.parametrize("name,window", WINDOW_APPEND_CASES)
+@pytest.mark.parametrize("split,psize", [(False, 0), (True, 512), (True, 32)])
+def test_window_append_matches_write_then_windowed_attend(P, name, window, split, psize):
+    case, _ = get_case(name)
+    if case.name == "long32k" and not split:
+        pytest.skip("the 32K single sequence is a split-KV workload")
+    ref, kc, vc = window_append_ref(name, window)
+    dc = DevCase(case)
+    out, k, v = run_window_append(P, dc, window, split=split, psize=psize or 512)
+    assert np.array_equal(dev_to_bits(k), kc), "key cache after the append differs"
+    assert np.array_equal(dev_to_bits(v), vc), "value cache after the append differs"
+    err = max_err(out, ref)
+    assert err <= 2e-4, f"{name}/{window}: fp32-out max abs err {err}"
+
+
+def test_window_append_agrees_with_the_two_call_step(P):
+    """kv_cache_write + the windowed split-KV call: same caches, outputs equal
+    up to fp32 summation order."""
+    case, _ = get_case("small_verify_q4")
+    dc = DevCase(case)
+    out_a, k_a, v_a = run_window_append(P, dc, 9, split=True, psize=32)
+    k, v = dc.k.clone(), dc.v.clone()
+    P.kv_cache_write(dc.new_k, dc.new_v, k, v, dc.slots)
+    out_b = run_window(P, dc, 9, split=True, psize=32, k=k, v=v)
+    assert torch.equal(k, k_a) and torch.equal(v, v_a)
+    assert (out_a - out_b).abs().max().item() <= 1e-5
+
+
 def test_window_zero_is_the_plain_decode(P):
     case, _ = get_case("small_verify_q4")
     dc = DevCase(case)
