@@ -657,6 +657,66 @@ def test_k8v4_append_agrees_with_the_two_call_step(P):
     assert (out_a - out_b).abs().max().item() <= 1e-5
 
 
+def test_k8v4_and_window_append_graph_replays_match_eager(P):
+    """The K8/V4 and windowed append forms captured in one HIP graph and
+    replayed several times from the same starting arrays, with eager work and
+    synchronisation between replays: every replay equals the eager results
+    bit for bit (outputs and arrays)."""
+    case, before, _, _ = get_k8v4_append_case("small_verify_q4")
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()      # noqa: E731
+    start = [dev(a) for a in before]
+    pool = [a.clone() for a in start]
+    q = bits_to_dev(case.query, case.fmt)
+    nk, nv = bits_to_dev(case.new_key, case.fmt), bits_to_dev(case.new_value, case.fmt)
+    bt, cl = dev(case.block_tables), dev(case.context_lens)
+    mcl = int(case.context_lens.max())
+    n = P.splitkv_workspace_size(*q.shape[:3], q.shape[3], mcl, 32)
+    ws1 = torch.zeros(n // 4 + 4, dtype=torch.float32, device="cuda")
+    ws2 = torch.zeros_like(ws1)
+    wcase, _ = get_case("small_verify_q4")
+    dc = DevCase(wcase)
+    k, v = dc.k.clone(), dc.v.clone()
+    outs = [torch.zeros(q.shape, dtype=torch.float32, device="cuda") for _ in range(2)]
+
+    def reset():
+        for a, b in zip(pool, start):
+            a.copy_(b)
+        k.copy_(dc.k)
+        v.copy_(dc.v)
+
+    def step():
+        P.paged_attention_decode_splitkv_k8v4_append(outs[0], q, nk, nv, *pool, bt, cl, case.scale,
+                                                     case.gqa_factor, mcl, 32, ws1)
+        P.paged_attention_decode_splitkv_window_append(outs[1], dc.q, dc.new_k, dc.new_v, k, v,
+                                                       dc.bt, dc.cl, wcase.scale,
+                                                       wcase.gqa_factor, 9, mcl, 32, ws2)
+
+    reset()
+    step()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs] + [a.clone() for a in pool] + [k.clone(), v.clone()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        reset()
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = list(outs) + list(pool) + [k, v]
+        for a, e in zip(got, eager):
+            assert torch.equal(a, e), f"replay {rep}"
+        run_decode(P, dc, split=False)                  # eager work between replays
+
+
 def test_k8v4_append_skips_new_tokens_without_a_pool_block(P):
     """A new token whose table entry names no pool block is neither quantized
     into the arrays nor attended."""
