@@ -14,7 +14,9 @@
 //   byte is read from HBM once.  The direct form is the same kernel with one
 //   partition per sequence; the split-KV form writes per-partition partials and
 //   a second kernel merges them by log-sum-exp.  The same kernel also runs
-//   the append form (the new tokens stored and attended as one more tile), the
+//   the append form (the new tokens stored into the cache at launch start and
+//   attended: patched into the last cache block when they share it, else as
+//   one more tile), the
 //   sliding window (partitions counted from the window's first block) and the
 //   two cascade passes (a group's rows stacked in one tile over its shared
 //   prefix; each sequence past its group's prefix).  The approximate sparse-V
@@ -28,7 +30,7 @@
 //     block max is reduced across the four quarters with two lane exchanges.
 //   - The probabilities are already in the B-operand layout of a 16x16x16 MFMA
 //     computing O^T = V^T P^T; they are split into a 16-bit high part and a
-//     16-bit remainder so the product keeps ~22 bits of each weight.
+//     16-bit remainder so the product keeps ~21 bits of each weight.
 //   - V rows are staged through LDS (natural [token][dim] layout) and read back
 //     transposed as the A operand.  Output lane l holds row l % 16's dims
 //     16n + 4*(l/16) + r, so the softmax rescale is one factor per lane.
@@ -49,11 +51,12 @@
 //    bf16 queries, the exact float of u truncated to bf16.  The constant offset
 //    (1152 or 128) times the row's query sum starts the score accumulator, so
 //    the scores come out exact (one MFMA pass per wave computes it).
-//  - V: each nibble, masked into an fp16 mantissa under 0x64, is 1024 + c; one
-//    packed fp16 subtract makes it c exactly.  The four mask shifts of a 32-bit
-//    word give the codes pairwise as (c0,c4), (c1,c5), (c2,c6), (c3,c7), and the
-//    V tile is staged in that order; the output dims are put back in order when
-//    the partial is written.  The PV products always run in fp16 (codes are
+//  - V: a nibble masked into fp16 mantissa bits 0..3 under exponent byte 0x64
+//    is 1024 + c, in bits 4..7 under 0x54 it is 64 + c; one packed fp16
+//    subtract makes it c exactly.  Two masks of a 32-bit word and of the word
+//    shifted by 8 give the codes pairwise as (c0,c4), (c1,c5), (c2,c6), (c3,c7),
+//    and the V tile is staged in that order; the output dims are put back in
+//    order when the partial is written.  The PV products always run in fp16 (codes are
 //    small integers; the weights are split hi/lo).
 
 #include <math.h>
@@ -74,9 +77,9 @@ __device__ __forceinline__ int qk_dim(int m, int qd) {
 }
 
 // Four int8 K codes (one 32-bit word) -> two words of 16-bit MFMA elements
-// holding off + c exactly (off = kK8Offset), in dim order.
-template <Fmt QT> constexpr float kK8Offset = QT == Fmt::F16 ? 1152.f : 128.f;
-// -off in both halves of a word: the operand that makes off * sum(q)
+// holding off + c exactly, in dim order: off = 1152 for fp16 queries, 128 for
+// bf16 ones.  kK8NegOffset2 is -off in both halves of a word (fp16 0xE480 =
+// -1152, bf16 0xC300 = -128): the operand that makes -off * sum(q).
 template <Fmt QT> constexpr uint32_t kK8NegOffset2 = QT == Fmt::F16 ? 0xE480E480u : 0xC300C300u;
 
 template <Fmt QT>
