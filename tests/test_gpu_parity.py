@@ -463,6 +463,19 @@ def test_append_long32k_bench_launch_configuration(P):
     assert np.array_equal(dev_to_bits(k), kc) and np.array_equal(dev_to_bits(v), vc)
 
 
+def test_spec_verify_append_bench_launch_configuration(P):
+    """The verify batch as the bench times it: all 64 sequences, append form,
+    split-KV partition 1024, bf16 output."""
+    case, _ = get_case("spec_verify")
+    ref, kc, vc = oracle.decode_append(case.query, case.new_key, case.new_value, case.key_cache,
+                                       case.value_cache, case.block_tables, case.context_lens,
+                                       case.scale, case.gqa_factor, case.fmt)
+    dc = DevCase(case)
+    out, k, v = run_append(P, dc, split=True, psize=1024, out_dtype=torch.bfloat16)
+    assert np.array_equal(dev_to_bits(k), kc) and np.array_equal(dev_to_bits(v), vc)
+    assert max_err(out, ref) <= TOL
+
+
 def test_append_agrees_with_the_two_call_step(P):
     """Same step through kv_cache_write + paged_attention_decode_splitkv: same
     caches bit for bit, outputs equal up to fp32 summation order."""
@@ -843,6 +856,17 @@ def test_window_append_matches_write_then_windowed_attend(P, name, window, split
     assert np.array_equal(dev_to_bits(v), vc), "value cache after the append differs"
     err = max_err(out, ref)
     assert err <= 2e-4, f"{name}/{window}: fp32-out max abs err {err}"
+
+
+def test_window_append_bench_launch_configuration(P):
+    """The 32K window-2048 step as the bench times it: append form, windowed
+    split-KV partition 128, fp16 output."""
+    ref, kc, vc = window_append_ref("long32k", 2048)
+    case, _ = get_case("long32k")
+    dc = DevCase(case)
+    out, k, v = run_window_append(P, dc, 2048, split=True, psize=128, out_dtype=torch.float16)
+    assert np.array_equal(dev_to_bits(k), kc) and np.array_equal(dev_to_bits(v), vc)
+    assert max_err(out, ref) <= TOL
 
 
 def test_window_append_agrees_with_the_two_call_step(P):
