@@ -250,7 +250,7 @@ OTHER = {
     "tiny": (1, 32, 0),
     "llama8b_batch": (2, 8, 0),
     "spec_verify": (4, 8, 1024),
-    "k8v4": (5, 8, 1024),
+    "k8v4": (5, 8, 2048),
     "long32k_window2048": (3, 32, 128),
 }
 WINDOW = {"long32k_window2048": 2048}       # sliding window of the windowed workloads

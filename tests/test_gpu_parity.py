@@ -640,9 +640,9 @@ def test_k8v4_append_matches_quantize_then_attend(P, name, split, psize):
 
 def test_k8v4_append_batch_launch_configuration(P):
     """The K8/V4 batch step as the bench times it: 16 x 8192 tokens, split-KV
-    partition 1024, fp16 output."""
+    partition 2048, fp16 output."""
     case, before, after, ref = get_k8v4_append_case("k8v4")
-    out, arrs = run_k8v4_append(P, case, before, split=True, psize=1024, out_dtype=torch.float16)
+    out, arrs = run_k8v4_append(P, case, before, split=True, psize=2048, out_dtype=torch.float16)
     assert_k8v4_arrays_equal(arrs, after)
     assert max_err(out, ref) <= TOL
 
