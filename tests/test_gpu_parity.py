@@ -1008,7 +1008,7 @@ CASCADE_CASES = {
 
 
 @pytest.mark.parametrize("name", list(CASCADE_CASES))
-@pytest.mark.parametrize("psize", [512, 32])
+@pytest.mark.parametrize("psize", [1024, 512, 32])
 def test_cascade_matches_oracle(P, name, psize):
     case = CASCADE_CASES[name]()
     ref = oracle_decode(case)
