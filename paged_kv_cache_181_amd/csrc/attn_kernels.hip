@@ -313,7 +313,27 @@ void attn_partition_kernel(const AttnArgs a) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int rho = lane & 15, qd = lane >> 4;
-  const int p = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // (partition, KV head, sequence) of this workgroup.  K8/V4 runs on a 1-D
+  // grid ordered so that every KV head of one (partition, sequence) lands on
+  // the same XCD (workgroups go to the eight XCDs round-robin in dispatch
+  // order): a 128-byte line of 4-bit V codes holds two heads' rows and a line
+  // of scales or zeros holds every head's, so within one L2 each such line
+  // comes from HBM once, not once per XCD that reads it.  Dispatch id
+  // 8 * (g + Hkv * (u / 8)) + u % 8 is head g of unit u = p + parts * b; the
+  // grid is rounded up to whole groups of eight units.
+  int p, g, b;
+  if constexpr (KV == Fmt::K8V4) {
+    const int id = (int)blockIdx.x, hk = a.num_kv_heads;
+    const int u = (id / (8 * hk)) * 8 + (id & 7);
+    if (u >= a.num_parts * a.batch) return;                 // past the last unit (whole group)
+    g = (id >> 3) % hk;
+    p = u % a.num_parts;
+    b = u / a.num_parts;
+  } else {
+    p = blockIdx.x;
+    g = blockIdx.y;
+    b = blockIdx.z;
+  }
   const int Q = a.q_len, G = a.gqa, GQ = G * Q, Hq = a.num_q_heads;
   const bool split = a.ws_o != nullptr;
   // Cascade passes over shared whole-block prefixes.  Prefix pass (PREFIX,
@@ -336,8 +356,10 @@ void attn_partition_kernel(const AttnArgs a) {
   // ---- loads that do not depend on the sequence length go out first and
   // together: the table entries of this wave's first blocks, this wave's copy
   // of the query rows, and the length.  Wave w owns the contiguous run of
-  // `per` blocks starting at bb + w*per (per depends on the partition size
-  // only, so a block's wave never depends on the length); lane j holds entry
+  // `per` blocks starting at bb + w*per (per is first taken from the
+  // partition size, so that a full partition's table chunk can be fetched
+  // before the length arrives; a shorter partition re-fetches it for its
+  // evenly spread runs further down); lane j holds entry
   // j of a 64-entry chunk of the run, picked out later with readlane, so no
   // table load sits between the K/V loads of consecutive blocks.  Nothing
   // waits on another wave before the first K/V loads.
@@ -422,11 +444,14 @@ void attn_partition_kernel(const AttnArgs a) {
     }
     return;
   }
-  if (b0 != bb_guess || be - bb > a.part_blocks) {
-    // partitions counted from a window's start, or a last partition longer
-    // than the others (length past the grid): the runs are spread evenly
-    // over the blocks actually read
-    per = (be - b0 + NW - 1) / NW;
+  if (const int per_fit = (be - b0 + NW - 1) / NW; b0 != bb_guess || per_fit != per) {
+    // a partition with fewer blocks than the partition size (the direct
+    // form, a sequence's last partition), partitions counted from a window's
+    // start, or a last partition longer than the others (length past the
+    // grid): the runs are spread evenly over the blocks actually read, so no
+    // wave idles while another walks a long run; the first table chunk is
+    // fetched again for the new runs
+    per = per_fit;
     const int e = b0 + w * per + lane;
     tbl_next = lane < per ? buf_load<int>(btr, (uint32_t)e * 4u) : 0;
   }
@@ -500,7 +525,6 @@ void attn_partition_kernel(const AttnArgs a) {
     const int64_t first = (int64_t)b * Q * a.num_kv_heads * D * 2;
     const auto kr = span_rsrc((const char*)a.new_k + first, rows_b);
     const auto vr = span_rsrc((const char*)a.new_v + first, rows_b);
-    const uint32_t row0 = (uint32_t)((rho * a.num_kv_heads + g) * D * 2);
     if constexpr (KV == Fmt::K8V4) {
       // quantized a token at a time with the wave spread over its dims (as the
       // quantize-on-write does), rows t >= q_len read as zeros
@@ -1260,8 +1284,15 @@ template <Fmt KV, Fmt QT, int D>
 static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream, int stage) {
   if (stage != STAGE_MERGE) {
     const int rows = (a.mode == 1 ? a.group_size : 1) * a.gqa * a.q_len;
-    const dim3 grid((unsigned)a.num_parts, (unsigned)a.num_kv_heads,
-                    (unsigned)(a.mode == 1 ? a.num_groups : a.batch));
+    dim3 grid((unsigned)a.num_parts, (unsigned)a.num_kv_heads,
+              (unsigned)(a.mode == 1 ? a.num_groups : a.batch));
+    if constexpr (KV == Fmt::K8V4) {     // 1-D, XCD-grouped order (see the kernel)
+      if (a.mode != 0) return hipErrorInvalidValue;
+      const int64_t units = (int64_t)a.num_parts * a.batch;
+      const int64_t n = 8 * (int64_t)a.num_kv_heads * ((units + 7) / 8);
+      if (n > 0x7fffffff) return hipErrorInvalidConfiguration;
+      grid = dim3((unsigned)n, 1u, 1u);
+    }
     if constexpr (KV != Fmt::K8V4) {
       if (a.mode == 1) {                 // cascade prefix pass: its own instantiation
         if (rows <= 4)
