@@ -946,6 +946,9 @@ __global__ __launch_bounds__((8 * kWave), 4) void attn_sparse_v_kernel(const Att
   using MM = Mma<KV>;
   using SM = AttnSmem<KV, D, 4>;
   constexpr int NW = 8, RT = 4, GB = D == 128 ? 3 : 4;   // GB: blocks per wave per round
+  // table entries per chunk: a whole number of rounds (63 or 64), so the
+  // blocks of one round never straddle two chunks
+  constexpr int CH = (kWave / GB) * GB;
   constexpr int KS = D / 32;
   constexpr int NT = D / 16;
   constexpr int QSTR = SM::QSTR;
@@ -990,8 +993,11 @@ __global__ __launch_bounds__((8 * kWave), 4) void attn_sparse_v_kernel(const Att
     }
     return;
   }
-  if (be - bb > a.part_blocks) {
-    per = (be - bb + NW - 1) / NW;
+  if (const int per_fit = (be - bb + NW - 1) / NW; per_fit != per) {
+    // runs spread evenly over the blocks the partition holds (shorter than
+    // the partition size, or a last partition longer than the others);
+    // per is workgroup-uniform, so every wave still runs the same rounds
+    per = per_fit;
     const int e = bb + w * per + lane;
     tbl_next = lane < per ? buf_load<int>(btr, (uint32_t)e * 4u) : 0;
   }
@@ -1004,16 +1010,16 @@ __global__ __launch_bounds__((8 * kWave), 4) void attn_sparse_v_kernel(const Att
   const int full_lim = L - Q + 1;
 
   int tblv = tbl_next;
-  if (64 < per) {
-    const int kk = 64 + lane;
-    tbl_next = kk < nmine ? buf_load<int>(btr, (uint32_t)(w0 + kk) * 4u) : 0;
+  if (CH < per) {
+    const int kk = CH + lane;
+    tbl_next = lane < CH && kk < nmine ? buf_load<int>(btr, (uint32_t)(w0 + kk) * 4u) : 0;
   }
   const LaneOffsets<KV, D> loff(a.num_kv_heads, g, rho, qd);
   const uint32_t kblk = loff.kblk;
   // K of run block j (zeros and no memory traffic past the run or for a table
   // entry outside the pool); returns the mask of tokens with data
   auto fetch_k = [&](int j, u4 (&kr)[KS]) -> uint32_t {
-    const int pb = __builtin_amdgcn_readlane(tblv, j & 63);
+    const int pb = __builtin_amdgcn_readlane(tblv, j % CH);
     const bool ok = j < nmine && pb >= 0 && (int64_t)pb < a.num_blocks;
     const auto kres = span_rsrc((const char*)a.k_cache + (int64_t)(ok ? pb : 0) * kblk,
                                 ok ? kblk : 0u);
@@ -1025,7 +1031,7 @@ __global__ __launch_bounds__((8 * kWave), 4) void attn_sparse_v_kernel(const Att
   };
   // V of run block j for the tokens in `need` only
   auto fetch_v = [&](int j, uint32_t need, u4 (&vr)[KS]) {
-    const int pb = __builtin_amdgcn_readlane(tblv, j & 63);
+    const int pb = __builtin_amdgcn_readlane(tblv, j % CH);
     const bool ok = need != 0u && pb >= 0 && (int64_t)pb < a.num_blocks;
     const auto vres = span_rsrc((const char*)a.v_cache + (int64_t)(ok ? pb : 0) * kblk,
                                 ok ? kblk : 0u);
@@ -1051,10 +1057,10 @@ __global__ __launch_bounds__((8 * kWave), 4) void attn_sparse_v_kernel(const Att
 
   for (int rd = 0; rd < rounds; ++rd) {
     const int k0 = rd * GB;
-    if (k0 > 0 && (k0 & 63) == 0) {                // next 64-entry chunk of the run
+    if (k0 > 0 && k0 % CH == 0) {                  // next chunk of the run
       tblv = tbl_next;
-      const int kk = k0 + 64 + lane;
-      tbl_next = kk < nmine ? buf_load<int>(btr, (uint32_t)(w0 + kk) * 4u) : 0;
+      const int kk = k0 + CH + lane;
+      tbl_next = lane < CH && kk < nmine ? buf_load<int>(btr, (uint32_t)(w0 + kk) * 4u) : 0;
     }
     u4 buf[GB][KS];
     uint32_t vm[GB];

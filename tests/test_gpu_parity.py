@@ -1077,7 +1077,8 @@ def visible_rows(case):
 def test_sparse_v_threshold_zero_is_exact(P, name):
     case, ref = get_case(name)
     dc = DevCase(case)
-    for psize in (512, 32):
+    # 16384: at 32K each wave's run is 128 blocks, past one table chunk
+    for psize in (512, 32, 16384):
         out, rows = run_sparse(P, dc, 0.0, psize=psize)
         assert max_err(out, ref) <= 2e-4
         assert rows == visible_rows(case)
