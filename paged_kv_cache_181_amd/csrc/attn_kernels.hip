@@ -242,12 +242,14 @@ __device__ __forceinline__ void load_block(const AttnArgs& a, int64_t pb, bool l
 
 // Workgroup shape: RT query rows per KV head tile (4 when G*q_len <= 4, else
 // 16).  The 16-bit 4-row form runs 8 wavefronts at 4 per SIMD (128 registers),
-// the K8/V4 4-row form 4 wavefronts at 4 per SIMD, and the 16-row forms,
-// which hold more per lane, 4 wavefronts at 3.
+// the K8/V4 4-row form and the 16-bit 16-row form 4 wavefronts at 4 per SIMD
+// (the 16-row form's LDS, merge included, stays under 40 KB so that four
+// workgroups share a CU), and the K8/V4 16-row form, which holds more per
+// lane, 4 wavefronts at 3.
 template <Fmt KV, int RT> struct Shape {
   static constexpr bool WIDE = RT == 4 && KV != Fmt::K8V4;
   static constexpr int NW = WIDE ? 8 : 4;
-  static constexpr int WAVES_PER_SIMD = RT == 4 ? 4 : 3;
+  static constexpr int WAVES_PER_SIMD = RT == 4 || KV != Fmt::K8V4 ? 4 : 3;
 };
 
 template <Fmt KV, int D, int RT>
@@ -257,7 +259,8 @@ struct AttnSmem {
   static constexpr int VT = 16 * D * 2;                    // one staged V tile (bytes)
   static constexpr int VST = NW * VT;
   static constexpr int SIDE = KV == Fmt::K8V4 ? NW * 16 * (1 + 2 * GR) * 4 : 0;
-  static constexpr int MO = NW * RT * D * 4;               // merge: per-wave outputs
+  static constexpr int EP = RT == 16 ? 2 : 1;              // merge passes over the head dims
+  static constexpr int MO = NW * RT * (D / EP) * 4;        // merge: per-wave outputs (one pass)
   static constexpr int LOOP = VST + SIDE;
   static constexpr int BYTES = LOOP > MO ? LOOP : MO;
   // append form: the new tokens' tile, parked from the start of the launch to
@@ -265,6 +268,9 @@ struct AttnSmem {
   static constexpr int STASH = RT * 4 * (int)sizeof(BlockRegs<KV, D>);
   static constexpr int BYTES_APPEND = LOOP + STASH > MO ? LOOP + STASH : MO;
   static constexpr int QSTR = D + 8;                       // halves per staged query row
+  // staged query copies: one per wave (no wave waits on another), or in the
+  // 16-row forms one shared copy (keeps their LDS under 40 KB)
+  static constexpr int QCOPIES = RT == 16 ? 1 : NW;
 };
 
 // Max over lanes l, l^16, l^32, l^48 (the four quarters) without the LDS path.
@@ -307,7 +313,7 @@ void attn_partition_kernel(const AttnArgs a) {
   constexpr int GR = SM::GR;
   constexpr int QSTR = SM::QSTR;
   __shared__ __align__(16) unsigned char smem[SM::BYTES_APPEND];
-  __shared__ __align__(16) uint16_t q_s[NW * RT * QSTR];
+  __shared__ __align__(16) uint16_t q_s[SM::QCOPIES * RT * QSTR];
   __shared__ float mm_s[NW][16], ml_s[NW][16];
 
   const int lane = threadIdx.x & 63;
@@ -653,14 +659,19 @@ void attn_partition_kernel(const AttnArgs a) {
     }
   }
 
-  // ---- stage the query rows in this wave's own LDS area
-  uint16_t* qw = q_s + w * RT * QSTR;
+  // ---- stage the query rows: into this wave's own LDS area, or (one shared
+  // copy) by wave 0, the others waiting at a workgroup barrier; either way
+  // the first K/V loads are already in flight
+  uint16_t* qw = q_s + (SM::QCOPIES == 1 ? 0 : w) * RT * QSTR;
+  if (SM::QCOPIES == NW || w == 0) {
 #pragma unroll
-  for (int u = 0; u < QPL; ++u) {
-    const int idx = lane + u * kWave;
-    if (idx < QCW) *(u4*)(qw + (idx / (D / 8)) * QSTR + 8 * (idx % (D / 8))) = qv[u];
+    for (int u = 0; u < QPL; ++u) {
+      const int idx = lane + u * kWave;
+      if (idx < QCW) *(u4*)(qw + (idx / (D / 8)) * QSTR + 8 * (idx % (D / 8))) = qv[u];
+    }
   }
-  wave_lds_fence();
+  if constexpr (SM::QCOPIES == 1) __syncthreads();
+  else wave_lds_fence();
   const uint16_t* qrow = qw + (row_ok ? rho : rho % GQ) * QSTR;   // this lane's operand row
   // start of every score accumulator: 0, or for K8/V4 -off * (the row's query
   // sum), which cancels the offset the converted K codes carry
@@ -874,47 +885,53 @@ void attn_partition_kernel(const AttnArgs a) {
     for (int n = 0; n < NT; ++n) o[n] += zacc[n / 2];
   }
 
-  // ---- merge the NW wavefronts of this workgroup (LDS reused)
-  __syncthreads();
+  // ---- merge the NW wavefronts of this workgroup (LDS reused), in EP passes
+  // over the head dims (the 16-row forms take two, which halves the LDS the
+  // merge needs)
+  constexpr int EP = SM::EP, DH = D / EP, NTH = NT / EP;
   float* mo = (float*)smem;
-  if (rho < RT && rho < GQT) {
-#pragma unroll
-    for (int n = 0; n < NT; ++n)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 4 * qd + r;              // output row within the tile
-        mo[(w * RT + rho) * D + 16 * n + (KV == Fmt::K8V4 ? v4_dim(i) : i)] = o[n][r];
-      }
-  }
   if (qd == 0) {
     mm_s[w][rho] = m_run;
     ml_s[w][rho] = l_run;
   }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < GQT * D; idx += NW * kWave) {
-    const int rr = idx / D, d = idx % D;
-    float M = kNegInf;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, mm_s[ww][rr]);
-    const float Mu = M == kNegInf ? 0.f : M;
-    float num = 0.f, den = 0.f;
+  for (int e = 0; e < EP; ++e) {
+    __syncthreads();                           // the block loop's, or the last pass's, reads done
+    if (rho < RT && rho < GQT) {
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      const float e = fast_exp2(mm_s[ww][rr] - Mu);
-      num += e * mo[(ww * RT + rr) * D + d];
-      den += e * ml_s[ww][rr];
+      for (int n = 0; n < NTH; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * qd + r;            // output row within the tile
+          mo[(w * RT + rho) * DH + 16 * n + (KV == Fmt::K8V4 ? v4_dim(i) : i)] = o[e * NTH + n][r];
+        }
     }
-    const int64_t orow = orow_of(rr);
-    if (orow < 0) continue;
-    if (split) {
-      const int64_t pi = orow * wsp + a.part_base + p;
-      a.ws_o[pi * D + d] = num;
-      if (d == 0) {
-        a.ws_m[pi] = M;
-        a.ws_l[pi] = den;
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < GQT * DH; idx += NW * kWave) {
+      const int rr = idx / DH, dh = idx % DH, d = e * DH + dh;
+      float M = kNegInf;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, mm_s[ww][rr]);
+      const float Mu = M == kNegInf ? 0.f : M;
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const float ew = fast_exp2(mm_s[ww][rr] - Mu);
+        num += ew * mo[(ww * RT + rr) * DH + dh];
+        den += ew * ml_s[ww][rr];
       }
-    } else {
-      store_out(a.out, (OutT)a.out_dtype, orow * D + d, den > 0.f ? num / den : 0.f);
+      const int64_t orow = orow_of(rr);
+      if (orow < 0) continue;
+      if (split) {
+        const int64_t pi = orow * wsp + a.part_base + p;
+        a.ws_o[pi * D + d] = num;
+        if (d == 0) {
+          a.ws_m[pi] = M;
+          a.ws_l[pi] = den;
+        }
+      } else {
+        store_out(a.out, (OutT)a.out_dtype, orow * D + d, den > 0.f ? num / den : 0.f);
+      }
     }
   }
 }
