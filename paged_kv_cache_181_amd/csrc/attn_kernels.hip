@@ -1313,7 +1313,9 @@ static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream, int stage)
       if (a.mode != 0) return hipErrorInvalidValue;
       const int64_t units = (int64_t)a.num_parts * a.batch;
       const int64_t n = 8 * (int64_t)a.num_kv_heads * ((units + 7) / 8);
-      if (n > 0x7fffffff) return hipErrorInvalidConfiguration;
+      // a launch covers fewer than 2^32 work-items per dimension
+      if (n * Shape<KV, 4>::NW * kWave > 0xffffffffLL || n * Shape<KV, 16>::NW * kWave > 0xffffffffLL)
+        return hipErrorInvalidConfiguration;
       grid = dim3((unsigned)n, 1u, 1u);
     }
     if constexpr (KV != Fmt::K8V4) {
