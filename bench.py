@@ -211,6 +211,32 @@ def measured_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
+def cpu_baseline_tiny_one_thread(W, seconds=2.0):
+    """The oracle on the tiny workload (one sequence of 256 tokens, 8/2
+    heads, D 64) with BLAS held to one thread: microseconds per call."""
+    import oracle
+    c = W.tiny()
+    try:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=1, user_api="blas")
+    except Exception:
+        limit = None
+    try:
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.paged_attention(c.query, c.key_cache, c.value_cache, c.block_tables,
+                                   c.context_lens, c.scale, c.gqa_factor, "f16")
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or reps >= 2000:
+                break
+    finally:
+        if limit is not None:
+            limit.unregister()
+    return {"us_per_call": round(el / reps * 1e6, 1), "cores": 1, "kind": "oracle",
+            "calls": reps, "threads_limited": limit is not None}
+
+
 def cpu_baseline(wl, seconds):
     """The oracle as it stands on layer 0 of the same workload, repeated until
     about ``seconds`` of host time; reported in the metric's unit (GB/s)."""
@@ -614,6 +640,9 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        if "other_workloads" in result:
+            result["other_workloads"]["tiny"]["cpu_oracle_one_thread"] = \
+                cpu_baseline_tiny_one_thread(W)
     print(json.dumps(result), flush=True)
 
 
