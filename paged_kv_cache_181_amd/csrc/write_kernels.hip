@@ -18,17 +18,22 @@ __global__ __launch_bounds__(256) void kv_write_kernel(const u4* __restrict__ ke
                                                        u4* __restrict__ key_cache,
                                                        u4* __restrict__ value_cache,
                                                        const int64_t* __restrict__ slots,
-                                                       int64_t num_slots, int row_vecs) {
+                                                       int64_t num_slots, int row_vecs,
+                                                       int stride) {
   const int64_t t = blockIdx.x;
-  const int64_t slot = slots[t];
-  if (slot < 0 || slot >= num_slots) return;          // skipped token
+  int64_t slot = slots[t];
   const u4* ks = key + t * row_vecs;
   const u4* vs = value + t * row_vecs;
-  u4* kd = key_cache + slot * row_vecs;
-  u4* vd = value_cache + slot * row_vecs;
-  for (int i = threadIdx.x; i < row_vecs; i += blockDim.x) {
-    kd[i] = ks[i];
-    vd[i] = vs[i];
+  for (int i = threadIdx.x; i < row_vecs; i += stride) {   // stride = the workgroup size
+    // the row's loads go out together with the slot's, not after it: the
+    // empty asm takes the loaded values and passes the slot through, so
+    // nothing that depends on the slot (the check, the destination) is
+    // placed above the loads and the two latencies overlap
+    const u4 kk = ks[i], vv = vs[i];
+    asm volatile("" : "+s"(slot) : "v"(kk), "v"(vv));
+    if (slot < 0 || slot >= num_slots) break;            // skipped token
+    key_cache[slot * row_vecs + i] = kk;
+    value_cache[slot * row_vecs + i] = vv;
   }
 }
 
@@ -39,7 +44,7 @@ hipError_t launch_kv_write(const void* key, const void* value, void* key_cache, 
   const int threads = row_vecs >= 256 ? 256 : ((row_vecs + 63) / 64) * 64;
   hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)num_tokens), dim3(threads), 0, stream,
                      (const u4*)key, (const u4*)value, (u4*)key_cache, (u4*)value_cache, slots,
-                     num_blocks * kBlock, row_vecs);
+                     num_blocks * kBlock, row_vecs, threads);
   return hipGetLastError();
 }
 
@@ -66,16 +71,17 @@ __global__ __launch_bounds__(256) void kv_write_k8v4_kernel(
   const int64_t t = unit / hkv;
   const int h = (int)(unit % hkv);
   const int64_t slot = slots[t];
-  if (slot < 0 || slot >= num_slots) return;
 
-  // this lane's elements: d = lane * E + e
+  // this lane's elements: d = lane * E + e (loaded together with the slot)
   float k[E], v[E];
   const int64_t src = (t * hkv + h) * D + lane * E;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     k[e] = IN == Fmt::F16 ? f16_bits_to_f32(key[src + e]) : bf16_bits_to_f32(key[src + e]);
     v[e] = IN == Fmt::F16 ? f16_bits_to_f32(value[src + e]) : bf16_bits_to_f32(value[src + e]);
+    asm volatile("" ::"v"(k[e]), "v"(v[e]));                // keeps the loads above the check
   }
+  if (slot < 0 || slot >= num_slots) return;                // skipped token
 
   // ---- K: symmetric int8, one scale per (token, head)
   float amax = 0.f;
