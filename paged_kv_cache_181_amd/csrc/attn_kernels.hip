@@ -1255,6 +1255,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
       lp[u] = wl[pp];
       op[u] = *(const f4*)(wo + (int64_t)pp * D + 4 * c);
     }
+    // every value passes through an empty asm here, so the compiler cannot
+    // sink a partition's o and l loads below the test of its m (it did for
+    // the first one, which cost a second dependent round trip)
+#pragma unroll
+    for (int u = 0; u < U; ++u) asm volatile("" : "+v"(mp[u]), "+v"(lp[u]), "+v"(op[u]));
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       // -inf: the partition saw nothing and its o was never written (it may
@@ -1262,11 +1267,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
       const bool use = p0 + u * NG < np && mp[u] != kNegInf;
       const float m_new = use ? fmaxf(m_t, mp[u]) : m_t;
       const float e_old = m_t == kNegInf ? 0.f : fast_exp2(m_t - m_new);
-      const float e_new = fast_exp2(mp[u] - m_new);
-      if (use) {
-        acc = acc * e_old + op[u] * e_new;
-        den = den * e_old + lp[u] * e_new;
-      }
+      const float e_new = use ? fast_exp2(mp[u] - m_new) : 0.f;
+      const f4 o_u = use ? op[u] : f4{0.f, 0.f, 0.f, 0.f};
+      const float l_u = use ? lp[u] : 0.f;
+      acc = acc * e_old + o_u * e_new;
+      den = den * e_old + l_u * e_new;
       m_t = m_new;
     }
   }
