@@ -267,6 +267,10 @@ struct AttnSmem {
   // the end of the block loop (lanes of rows rho < RT), after the loop area
   static constexpr int STASH = RT * 4 * (int)sizeof(BlockRegs<KV, D>);
   static constexpr int BYTES_APPEND = LOOP + STASH > MO ? LOOP + STASH : MO;
+  // head-pair form: a parked tile per head, and more than half of a CU's
+  // 160 KB, so that one workgroup runs per CU
+  static constexpr int BYTES_PAIR_USED = LOOP + 2 * STASH > MO ? LOOP + 2 * STASH : MO;
+  static constexpr int BYTES_PAIR = BYTES_PAIR_USED > 82 * 1024 ? BYTES_PAIR_USED : 82 * 1024;
   static constexpr int QSTR = D + 8;                       // halves per staged query row
   // staged query copies: one per wave (no wave waits on another), or in the
   // 16-row forms one shared copy (keeps their LDS under 40 KB)
@@ -302,22 +306,31 @@ __device__ __forceinline__ u2 lds_read_tr16(const unsigned char* p) {
 // then at most 2^8, well inside fp16/bf16 range.
 constexpr float kRescaleSlack = 8.f;
 
-template <Fmt KV, Fmt QT, int D, int RT, bool PREFIX>
+// HP: KV heads per workgroup.  1: the workgroup's NW waves share one head and
+// split its partition into runs.  2 (16-bit caches, plain mode): waves
+// 0..NW/2-1 take head 2*blockIdx.y and the others the next head, each half
+// splitting the same partition; a token row's two heads (512 contiguous bytes)
+// are then read together, and one workgroup runs per CU.
+template <Fmt KV, Fmt QT, int D, int RT, bool PREFIX, int HP = 1>
 __global__ __launch_bounds__((Shape<KV, RT>::NW * kWave), (Shape<KV, RT>::WAVES_PER_SIMD))
 void attn_partition_kernel(const AttnArgs a) {
   using MM = Mma<QT>;
   using SM = AttnSmem<KV, D, RT>;
   constexpr int NW = SM::NW;
+  constexpr int NWH = NW / HP;         // waves per head
+  static_assert(HP == 1 || (HP == 2 && !PREFIX && KV != Fmt::K8V4 && RT == 4),
+                "head pairs: 16-bit caches, 4-row tiles, plain mode");
   constexpr int KS = D / 32;           // QK MFMA steps
   constexpr int NT = D / 16;           // PV output tiles
   constexpr int GR = SM::GR;
   constexpr int QSTR = SM::QSTR;
-  __shared__ __align__(16) unsigned char smem[SM::BYTES_APPEND];
+  __shared__ __align__(16) unsigned char smem[HP == 2 ? SM::BYTES_PAIR : SM::BYTES_APPEND];
   __shared__ __align__(16) uint16_t q_s[SM::QCOPIES * RT * QSTR];
   __shared__ float mm_s[NW][16], ml_s[NW][16];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  const int hw = w / NWH, wh = w % NWH;   // this wave's head within the workgroup, and its run
   const int rho = lane & 15, qd = lane >> 4;
   // (partition, KV head, sequence) of this workgroup.  K8/V4 runs on a 1-D
   // grid ordered so that every KV head of one (partition, sequence) lands on
@@ -337,9 +350,10 @@ void attn_partition_kernel(const AttnArgs a) {
     b = u / a.num_parts;
   } else {
     p = blockIdx.x;
-    g = blockIdx.y;
+    g = blockIdx.y * HP + hw;
     b = blockIdx.z;
   }
+  const int g0 = g - hw;                                    // the workgroup's first head
   const int Q = a.q_len, G = a.gqa, GQ = G * Q, Hq = a.num_q_heads;
   const bool split = a.ws_o != nullptr;
   // Cascade passes over shared whole-block prefixes.  Prefix pass (PREFIX,
@@ -352,11 +366,12 @@ void attn_partition_kernel(const AttnArgs a) {
   const int S = PREFIX ? a.group_size : 1;
   const int GQT = S * GQ;                                   // tile rows that belong to sequences
   // output (= query) row of tile row rr < GQT, or -1 for an empty member slot
-  auto orow_of = [&](int rr) -> int64_t {
+  auto orow_head = [&](int rr, int gg) -> int64_t {
     const int m = rr / GQ, rq = rr - m * GQ;
     const int bm = PREFIX ? a.grp_members[(int64_t)b * S + m] : b;
-    return bm < 0 ? -1 : ((int64_t)bm * Q + rq / G) * Hq + g * G + rq % G;
+    return bm < 0 ? -1 : ((int64_t)bm * Q + rq / G) * Hq + gg * G + rq % G;
   };
+  auto orow_of = [&](int rr) -> int64_t { return orow_head(rr, g); };
   const int64_t wsp = a.ws_parts;                           // partition slots per row
 
   // ---- loads that do not depend on the sequence length go out first and
@@ -375,10 +390,10 @@ void attn_partition_kernel(const AttnArgs a) {
   const auto btr = span_rsrc(a.block_tables + (int64_t)max(tab_b, 0) * a.max_blocks,
                              (uint32_t)a.max_blocks * 4u);
   const int bb_guess = p * a.part_blocks;       // the partition's first block without a window
-  int per = (a.part_blocks + NW - 1) / NW;
+  int per = (a.part_blocks + NWH - 1) / NWH;
   int tbl_next;
   {
-    const int e = bb_guess + w * per + lane;
+    const int e = bb_guess + wh * per + lane;
     tbl_next = lane < per ? buf_load<int>(btr, (uint32_t)e * 4u) : 0;
   }
   constexpr int QCW = RT * (D / 8);                         // 16-byte query chunks per wave
@@ -441,8 +456,8 @@ void attn_partition_kernel(const AttnArgs a) {
   if (split && b0 >= be && p != p_new) {                    // partition with nothing to read:
     // mark it empty (max -inf, sum 0) so the merge can read every partition
     // without first reading the sequence length
-    for (int rr = threadIdx.x; rr < GQT; rr += NW * kWave) {
-      const int64_t orow = orow_of(rr);
+    for (int rr = threadIdx.x; rr < HP * GQT; rr += NW * kWave) {
+      const int64_t orow = orow_head(rr % GQT, g0 + rr / GQT);
       if (orow < 0) continue;
       const int64_t pi = orow * wsp + a.part_base + p;
       a.ws_m[pi] = kNegInf;
@@ -450,7 +465,7 @@ void attn_partition_kernel(const AttnArgs a) {
     }
     return;
   }
-  if (const int per_fit = (be - b0 + NW - 1) / NW; b0 != bb_guess || per_fit != per) {
+  if (const int per_fit = (be - b0 + NWH - 1) / NWH; b0 != bb_guess || per_fit != per) {
     // a partition with fewer blocks than the partition size (the direct
     // form, a sequence's last partition), partitions counted from a window's
     // start, or a last partition longer than the others (length past the
@@ -458,10 +473,10 @@ void attn_partition_kernel(const AttnArgs a) {
     // wave idles while another walks a long run; the first table chunk is
     // fetched again for the new runs
     per = per_fit;
-    const int e = b0 + w * per + lane;
+    const int e = b0 + wh * per + lane;
     tbl_next = lane < per ? buf_load<int>(btr, (uint32_t)e * 4u) : 0;
   }
-  const int w0 = b0 + w * per;                              // first block of this wave's run
+  const int w0 = b0 + wh * per;                             // first block of this wave's run
   const int nmine = max(0, min(per, be - w0));
 
   // the query row this lane owns: rho = iq * G + hl, or in the prefix pass
@@ -522,7 +537,7 @@ void attn_partition_kernel(const AttnArgs a) {
   const int new_row0 = (L - Q) & (kBlock - 1);              // the first new token's row
   const bool patch = append && L - Q > 0 && new_row0 != 0 && (L - Q) / kBlock == blk_new;
   const bool app_wave = append && p == p_new &&
-                        w == (patch ? (blk_new - b0) / max(per, 1) : NW - 1);   // wave-uniform
+                        wh == (patch ? (blk_new - b0) / max(per, 1) : NWH - 1);   // wave-uniform
   u4 nkh[D / 32], nvh[D / 32];        // 16-bit: this lane's new-row halves, 8 per u4
   uint32_t nkw[RT], nvw[RT];          // K8/V4: token t's halves of dims lane*E .. +E-1
   constexpr int E = D / kWave;        // K8/V4 quantization: dims per lane and token
@@ -554,7 +569,7 @@ void attn_partition_kernel(const AttnArgs a) {
   }
   BlockRegs<KV, D> r0, r1;
   uint32_t ok0 = fetch(0, 0, min(64, nmine), r0), ok1 = 0u;
-  unsigned char* stash = smem + SM::LOOP;
+  unsigned char* stash = smem + SM::LOOP + hw * SM::STASH;   // this head's parked tile
   const bool tv = tnew >= 0 && (int64_t)tnew < a.num_blocks;   // rho < Q, position >= 0
   if (app_wave) {
     if constexpr (KV != Fmt::K8V4) {
@@ -907,20 +922,21 @@ void attn_partition_kernel(const AttnArgs a) {
         }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < GQT * DH; idx += NW * kWave) {
-      const int rr = idx / DH, dh = idx % DH, d = e * DH + dh;
+    for (int idx = threadIdx.x; idx < HP * GQT * DH; idx += NW * kWave) {
+      const int hh = idx / (GQT * DH), rem = idx % (GQT * DH);   // head within the workgroup
+      const int rr = rem / DH, dh = rem % DH, d = e * DH + dh;
       float M = kNegInf;
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, mm_s[ww][rr]);
+      for (int ww = hh * NWH; ww < (hh + 1) * NWH; ++ww) M = fmaxf(M, mm_s[ww][rr]);
       const float Mu = M == kNegInf ? 0.f : M;
       float num = 0.f, den = 0.f;
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
+      for (int ww = hh * NWH; ww < (hh + 1) * NWH; ++ww) {
         const float ew = fast_exp2(mm_s[ww][rr] - Mu);
         num += ew * mo[(ww * RT + rr) * DH + dh];
         den += ew * ml_s[ww][rr];
       }
-      const int64_t orow = orow_of(rr);
+      const int64_t orow = orow_head(rr, g0 + hh);
       if (orow < 0) continue;
       if (split) {
         const int64_t pi = orow * wsp + a.part_base + p;
@@ -1308,6 +1324,19 @@ static hipError_t launch_merge(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Compute units of the current device (0 if unknown), read once per device.
+static int device_cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = -1;
+    cached[dev] = n;
+  }
+  return cached[dev] > 0 ? cached[dev] : 0;
+}
+
 template <Fmt KV, Fmt QT, int D>
 static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream, int stage) {
   if (stage != STAGE_MERGE) {
@@ -1336,7 +1365,23 @@ static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream, int stage)
         return launch_merge<D>(a, stream);
       }
     }
-    if (rows <= 4) {
+    // Head pairs when the one-head grid needs more than one workgroup per CU
+    // and the pair grid fits in one (the 32K sequence: 512 workgroups become
+    // 256).  A smaller grid keeps one head per workgroup: pairs would leave
+    // CUs idle, and one CU alone streams far below its share of HBM.
+    bool pairs = false;
+    if constexpr (KV != Fmt::K8V4) {
+      const int64_t wgs = (int64_t)a.num_parts * a.num_kv_heads * a.batch;
+      const int cus = device_cu_count();
+      pairs = rows <= 4 && a.mode == 0 && a.num_kv_heads % 2 == 0 && wgs > cus && wgs <= 2 * (int64_t)cus;
+    }
+    if (pairs) {
+      if constexpr (KV != Fmt::K8V4) {
+        const dim3 pgrid((unsigned)a.num_parts, (unsigned)(a.num_kv_heads / 2), (unsigned)a.batch);
+        hipLaunchKernelGGL((attn_partition_kernel<KV, QT, D, 4, false, 2>), pgrid,
+                           dim3(Shape<KV, 4>::NW * kWave), 0, stream, a);
+      }
+    } else if (rows <= 4) {
       hipLaunchKernelGGL((attn_partition_kernel<KV, QT, D, 4, false>), grid,
                          dim3(Shape<KV, 4>::NW * kWave), 0, stream, a);
     } else {

@@ -53,6 +53,12 @@ CASES = {
     "small_g16": lambda: small(106, num_q_heads=16, num_kv_heads=1, head_dim=64),
     "edge_lengths": lambda: small(107, batch=8, q_len=2, num_q_heads=8, num_kv_heads=2, head_dim=128,
                                   lengths=[0, 1, 2, 15, 16, 17, 32, 33]),
+    # at partition 512 these run 8 x 8 x 5 = 320 one-head workgroups, more
+    # than one per CU of a 256-CU device, so they take the head-pair form
+    "pairs_b5": lambda: small(108, batch=5, q_len=1, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                              fmt="bf16", lengths=[4096, 3000, 3900, 2500, 3521]),
+    "pairs_q2_d64": lambda: small(109, batch=5, q_len=2, num_q_heads=16, num_kv_heads=8,
+                                  head_dim=64, lengths=[4096, 4000, 1234, 3333, 2049]),
 }
 
 _cache = {}
@@ -401,6 +407,8 @@ APPEND_CASES = {
                                         lengths=[515, 512, 36, 32, 4, 3]),
     "llama8b_batch": lambda: W.llama8b_batch(),
     "spec_verify_b8": lambda: W.spec_verify(batch=8),
+    "pairs_b5": CASES["pairs_b5"],
+    "pairs_q2_d64": CASES["pairs_q2_d64"],
     "long32k": lambda: W.long32k(),
 }
 
@@ -753,6 +761,7 @@ WINDOW_CASES = [
     ("small_f16_d64", 100), ("small_bf16_d128_g4", 33), ("small_verify_q4", 1),
     ("small_verify_q4", 5), ("small_verify_q4", 40), ("small_g8_q2", 7), ("edge_lengths", 2),
     ("edge_lengths", 16), ("long32k", 2048), ("long32k", 4000),
+    ("pairs_b5", 3900), ("pairs_q2_d64", 3800),     # head pairs at partition 512
 ]
 _window_refs = {}
 
@@ -803,7 +812,7 @@ def test_window_matches_oracle(P, name, window, split, psize):
 WINDOW_APPEND_CASES = [
     ("small_f16_d64", 1), ("small_f16_d64", 17), ("small_bf16_d128_g4", 33),
     ("small_verify_q4", 5), ("small_g8_q2", 7), ("edge_lengths", 2), ("edge_lengths", 16),
-    ("long32k", 2048),
+    ("long32k", 2048), ("pairs_b5", 3900), ("pairs_q2_d64", 3800),
 ]
 _window_append_refs = {}
 
