@@ -606,7 +606,7 @@ def main():
         "decode_tokens_per_s": round(1e3 / ms, 2),
         "roofline": {
             "bound": "hbm",
-            "kernel": "attn_partition_kernel<F16,F16,128,4>",
+            "kernel": "attn_partition_kernel<F16,F16,128,4> (head-pair form)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
