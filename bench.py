@@ -274,7 +274,7 @@ OTHER = {
     # partition is the caller's choice for these batches: the fastest of a
     # sweep over direct, 256, 512, 1024 and 2048 on MI355X
     "tiny": (1, 32, 0),
-    "llama8b_batch": (2, 8, 0),
+    "llama8b_batch": (2, 8, 2048),
     "spec_verify": (4, 8, 1024),
     "k8v4": (5, 8, 2048),
     "long32k_window2048": (3, 32, 128),

@@ -471,6 +471,17 @@ def test_append_long32k_bench_launch_configuration(P):
     assert np.array_equal(dev_to_bits(k), kc) and np.array_equal(dev_to_bits(v), vc)
 
 
+def test_llama8b_append_bench_launch_configuration(P):
+    """The Llama-3-8B-shaped batch as the bench times it: all 32 sequences,
+    append form, split-KV partition 2048 (512 one-head workgroups, so the
+    head-pair form runs), bf16 output."""
+    case, (ref, kc, vc) = get_append_case("llama8b_batch")
+    dc = DevCase(case)
+    out, k, v = run_append(P, dc, split=True, psize=2048, out_dtype=torch.bfloat16)
+    assert np.array_equal(dev_to_bits(k), kc) and np.array_equal(dev_to_bits(v), vc)
+    assert max_err(out, ref) <= TOL
+
+
 def test_spec_verify_append_bench_launch_configuration(P):
     """The verify batch as the bench times it: all 64 sequences, append form,
     split-KV partition 1024, bf16 output."""
