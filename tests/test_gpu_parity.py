@@ -59,6 +59,9 @@ CASES = {
                               fmt="bf16", lengths=[4096, 3000, 3900, 2500, 3521]),
     "pairs_q2_d64": lambda: small(109, batch=5, q_len=2, num_q_heads=16, num_kv_heads=8,
                                   head_dim=64, lengths=[4096, 4000, 1234, 3333, 2049]),
+    # direct form (and one 512-token partition): 40 x 8 = 320 one-head workgroups
+    "pairs_direct_b40": lambda: small(110, batch=40, q_len=1, num_q_heads=32, num_kv_heads=8,
+                                      head_dim=64),
 }
 
 _cache = {}
@@ -409,6 +412,7 @@ APPEND_CASES = {
     "spec_verify_b8": lambda: W.spec_verify(batch=8),
     "pairs_b5": CASES["pairs_b5"],
     "pairs_q2_d64": CASES["pairs_q2_d64"],
+    "pairs_direct_b40": CASES["pairs_direct_b40"],
     "long32k": lambda: W.long32k(),
 }
 
