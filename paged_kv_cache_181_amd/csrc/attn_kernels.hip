@@ -11,7 +11,9 @@
 //   grid = (partition, KV head, sequence); a workgroup of NW wavefronts owns the
 //   blocks of one partition; wavefront w takes a contiguous run of them.  All
 //   G*q_len query rows that share a KV head live in one wavefront, so each K/V
-//   byte is read from HBM once.  The direct form is the same kernel with one
+//   byte is read from HBM once.  In the head-pair form a workgroup takes two
+//   KV heads, half of its wavefronts each (grid = (partition, head pair,
+//   sequence)); it runs when that brings the grid down to one workgroup per CU.  The direct form is the same kernel with one
 //   partition per sequence; the split-KV form writes per-partition partials and
 //   a second kernel merges them by log-sum-exp.  The same kernel also runs
 //   the append form (the new tokens stored into the cache at launch start and
