@@ -379,7 +379,8 @@ void attn_partition_kernel(const AttnArgs a) {
   // ---- loads that do not depend on the sequence length go out first and
   // together: the table entries of this wave's first blocks, this wave's copy
   // of the query rows, and the length.  Wave w owns the contiguous run of
-  // `per` blocks starting at bb + w*per (per is first taken from the
+  // `per` blocks starting at bb + wh*per (wh: w counted within its head's
+  // waves, so w itself with one head per workgroup; per is first taken from the
   // partition size, so that a full partition's table chunk can be fetched
   // before the length arrives; a shorter partition re-fetches it for its
   // evenly spread runs further down); lane j holds entry
