@@ -297,3 +297,57 @@ def test_cascade_workspace_and_errors(P):
     bad = ok_tail.copy()
     bad[4] = -16
     assert lib.paged_attention_decode_cascade(*base, *bad, None) == -2
+
+
+# ------------------------------------------------------------ argument fuzzing
+#
+# Arbitrary sizes with every pointer NULL: each call must return a defined
+# error code (or succeed as a no-op for an empty batch) and never reach a
+# launch.  NULL pointers fail validation before any HIP call, so nothing can
+# be launched whatever the sizes are.
+
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+_any_int = st.one_of(st.integers(-3, 70), st.sampled_from([64, 128, 256, 4096, 65535, 65536,
+                                                             1 << 26, (1 << 26) + 1, 2**31 - 1]))
+_NO_LAUNCH = {0, -1, -2, -3, -4, -6}
+
+
+@settings(max_examples=400, deadline=None)
+@given(out_dtype=st.integers(-1, 4), kv_dtype=st.integers(-1, 4), mb=_any_int, batch=_any_int,
+       q_len=_any_int, hq=_any_int, g=_any_int, d=_any_int, bs=_any_int, nb=_any_int,
+       scale=st.sampled_from([0.088, 0.0, -1.0, float("inf"), float("nan")]))
+def test_attention_validation_never_launches(P, out_dtype, kv_dtype, mb, batch, q_len, hq, g, d,
+                                             bs, nb, scale):
+    rc = P.lib.paged_attention_decode(None, out_dtype, None, None, None, kv_dtype, None, mb, None,
+                                      batch, q_len, hq, g, d, bs, nb, scale, None)
+    assert rc in _NO_LAUNCH, (rc, P.last_error())
+    assert rc != 0 or batch == 0
+
+
+@settings(max_examples=300, deadline=None)
+@given(batch=_any_int, q_len=_any_int, hq=_any_int, g=_any_int, d=_any_int, mcl=_any_int,
+       part=_any_int, ws_bytes=st.sampled_from([0, 16, 1 << 20, 2**40]))
+def test_splitkv_validation_never_launches(P, batch, q_len, hq, g, d, mcl, part, ws_bytes):
+    rc = P.lib.paged_attention_decode_splitkv(None, 0, None, None, None, 0, None, 64, None, batch,
+                                              q_len, hq, g, d, 16, 64, 0.088, mcl, part, None,
+                                              ws_bytes, None)
+    assert rc in _NO_LAUNCH, (rc, P.last_error())
+    assert rc != 0 or batch == 0
+    size = ctypes.c_size_t(0)
+    rc = P.lib.paged_attention_decode_splitkv_workspace_size(batch, q_len, hq, d, mcl, part,
+                                                             ctypes.byref(size))
+    assert rc in _NO_LAUNCH, (rc, P.last_error())
+
+
+@settings(max_examples=300, deadline=None)
+@given(tokens=_any_int, hkv=_any_int, d=_any_int, bs=_any_int, nb=_any_int,
+       dtype=st.integers(-1, 4))
+def test_write_validation_never_launches(P, tokens, hkv, d, bs, nb, dtype):
+    rc = P.lib.kv_cache_write(None, None, None, None, None, tokens, hkv, d, bs, nb, dtype, None)
+    assert rc in _NO_LAUNCH, (rc, P.last_error())
+    assert rc != 0 or tokens == 0
+    rc = P.lib.kv_cache_write_k8v4(None, None, dtype, None, None, None, None, None, None, tokens,
+                                   hkv, d, bs, nb, None)
+    assert rc in _NO_LAUNCH, (rc, P.last_error())
+    assert rc != 0 or tokens == 0
