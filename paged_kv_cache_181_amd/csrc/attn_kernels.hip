@@ -11,9 +11,10 @@
 //   grid = (partition, KV head, sequence); a workgroup of NW wavefronts owns the
 //   blocks of one partition; wavefront w takes a contiguous run of them.  All
 //   G*q_len query rows that share a KV head live in one wavefront, so each K/V
-//   byte is read from HBM once.  In the head-pair form a workgroup takes two
-//   KV heads, half of its wavefronts each (grid = (partition, head pair,
-//   sequence)); it runs when that brings the grid down to one workgroup per CU.  The direct form is the same kernel with one
+//   byte is read from HBM once.  In the head-pair and head-quad forms a
+//   workgroup takes two or four KV heads, an equal share of its wavefronts
+//   each (grid = (partition, head group, sequence)); they run when that
+//   brings the grid down to one workgroup per CU.  The direct form is the same kernel with one
 //   partition per sequence; the split-KV form writes per-partition partials and
 //   a second kernel merges them by log-sum-exp.  The same kernel also runs
 //   the append form (the new tokens stored into the cache at launch start and
@@ -269,10 +270,12 @@ struct AttnSmem {
   // the end of the block loop (lanes of rows rho < RT), after the loop area
   static constexpr int STASH = RT * 4 * (int)sizeof(BlockRegs<KV, D>);
   static constexpr int BYTES_APPEND = LOOP + STASH > MO ? LOOP + STASH : MO;
-  // head-pair form: a parked tile per head, and more than half of a CU's
-  // 160 KB, so that one workgroup runs per CU
-  static constexpr int BYTES_PAIR_USED = LOOP + 2 * STASH > MO ? LOOP + 2 * STASH : MO;
-  static constexpr int BYTES_PAIR = BYTES_PAIR_USED > 82 * 1024 ? BYTES_PAIR_USED : 82 * 1024;
+  // forms with HP > 1 heads per workgroup: a parked tile per head, and more
+  // than half of a CU's 160 KB, so that one workgroup runs per CU
+  template <int HP> static constexpr int bytes_group() {
+    constexpr int used = LOOP + HP * STASH > MO ? LOOP + HP * STASH : MO;
+    return used > 82 * 1024 ? used : 82 * 1024;
+  }
   static constexpr int QSTR = D + 8;                       // halves per staged query row
   // staged query copies: one per wave (no wave waits on another), or in the
   // 16-row forms one shared copy (keeps their LDS under 40 KB)
@@ -309,9 +312,9 @@ __device__ __forceinline__ u2 lds_read_tr16(const unsigned char* p) {
 constexpr float kRescaleSlack = 8.f;
 
 // HP: KV heads per workgroup.  1: the workgroup's NW waves share one head and
-// split its partition into runs.  2 (16-bit caches, plain mode): waves
-// 0..NW/2-1 take head 2*blockIdx.y and the others the next head, each half
-// splitting the same partition; a token row's two heads (512 contiguous bytes)
+// split its partition into runs.  2 or 4 (16-bit caches, plain mode): waves
+// hw*NW/HP .. take head HP*blockIdx.y + hw, each group splitting the same
+// partition; a token row's HP heads (HP * 256 contiguous bytes at D = 128)
 // are then read together, and one workgroup runs per CU.
 template <Fmt KV, Fmt QT, int D, int RT, bool PREFIX, int HP = 1>
 __global__ __launch_bounds__((Shape<KV, RT>::NW * kWave), (Shape<KV, RT>::WAVES_PER_SIMD))
@@ -320,13 +323,13 @@ void attn_partition_kernel(const AttnArgs a) {
   using SM = AttnSmem<KV, D, RT>;
   constexpr int NW = SM::NW;
   constexpr int NWH = NW / HP;         // waves per head
-  static_assert(HP == 1 || (HP == 2 && !PREFIX && KV != Fmt::K8V4 && RT == 4),
+  static_assert(HP == 1 || ((HP == 2 || HP == 4) && !PREFIX && KV != Fmt::K8V4 && RT == 4),
                 "head pairs: 16-bit caches, 4-row tiles, plain mode");
   constexpr int KS = D / 32;           // QK MFMA steps
   constexpr int NT = D / 16;           // PV output tiles
   constexpr int GR = SM::GR;
   constexpr int QSTR = SM::QSTR;
-  __shared__ __align__(16) unsigned char smem[HP == 2 ? SM::BYTES_PAIR : SM::BYTES_APPEND];
+  __shared__ __align__(16) unsigned char smem[HP > 1 ? SM::template bytes_group<HP>() : SM::BYTES_APPEND];
   __shared__ __align__(16) uint16_t q_s[SM::QCOPIES * RT * QSTR];
   __shared__ float mm_s[NW][16], ml_s[NW][16];
 
@@ -1368,21 +1371,29 @@ static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream, int stage)
         return launch_merge<D>(a, stream);
       }
     }
-    // Head pairs when the one-head grid needs more than one workgroup per CU
-    // and the pair grid fits in one (the 32K sequence: 512 workgroups become
-    // 256).  A smaller grid keeps one head per workgroup: pairs would leave
-    // CUs idle, and one CU alone streams far below its share of HBM.
-    bool pairs = false;
+    // Head pairs (quads) when the one-head grid needs two (up to four)
+    // workgroups per CU and the grouped grid fits in one: the 32K sequence's
+    // 512 workgroups become 256 pairs.  A smaller grid keeps one head per
+    // workgroup: grouping would leave CUs idle, and one CU alone streams far
+    // below its share of HBM.
+    int hp = 1;
     if constexpr (KV != Fmt::K8V4) {
       const int64_t wgs = (int64_t)a.num_parts * a.num_kv_heads * a.batch;
-      const int cus = device_cu_count();
-      pairs = rows <= 4 && a.mode == 0 && a.num_kv_heads % 2 == 0 && wgs > cus && wgs <= 2 * (int64_t)cus;
+      const int64_t cus = device_cu_count();
+      if (rows <= 4 && a.mode == 0 && cus > 0 && wgs > cus) {
+        if (a.num_kv_heads % 2 == 0 && wgs <= 2 * cus) hp = 2;
+        else if (a.num_kv_heads % 4 == 0 && wgs <= 4 * cus) hp = 4;
+      }
     }
-    if (pairs) {
+    if (hp > 1) {
       if constexpr (KV != Fmt::K8V4) {
-        const dim3 pgrid((unsigned)a.num_parts, (unsigned)(a.num_kv_heads / 2), (unsigned)a.batch);
-        hipLaunchKernelGGL((attn_partition_kernel<KV, QT, D, 4, false, 2>), pgrid,
-                           dim3(Shape<KV, 4>::NW * kWave), 0, stream, a);
+        const dim3 hgrid((unsigned)a.num_parts, (unsigned)(a.num_kv_heads / hp), (unsigned)a.batch);
+        if (hp == 2)
+          hipLaunchKernelGGL((attn_partition_kernel<KV, QT, D, 4, false, 2>), hgrid,
+                             dim3(Shape<KV, 4>::NW * kWave), 0, stream, a);
+        else
+          hipLaunchKernelGGL((attn_partition_kernel<KV, QT, D, 4, false, 4>), hgrid,
+                             dim3(Shape<KV, 4>::NW * kWave), 0, stream, a);
       }
     } else if (rows <= 4) {
       hipLaunchKernelGGL((attn_partition_kernel<KV, QT, D, 4, false>), grid,
