@@ -929,15 +929,19 @@ void attn_partition_kernel(const AttnArgs a) {
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < HP * GQT * DH; idx += NW * kWave) {
-      const int hh = idx / (GQT * DH), rem = idx % (GQT * DH);   // head within the workgroup
+      const int hh = HP == 1 ? 0 : idx / (GQT * DH);              // head within the workgroup
+      const int rem = HP == 1 ? idx : idx - hh * (GQT * DH);
       const int rr = rem / DH, dh = rem % DH, d = e * DH + dh;
+      // constant trip counts, so the loops unroll and the LDS reads of all
+      // of the head's waves go out together
       float M = kNegInf;
 #pragma unroll
-      for (int ww = hh * NWH; ww < (hh + 1) * NWH; ++ww) M = fmaxf(M, mm_s[ww][rr]);
+      for (int j = 0; j < NWH; ++j) M = fmaxf(M, mm_s[hh * NWH + j][rr]);
       const float Mu = M == kNegInf ? 0.f : M;
       float num = 0.f, den = 0.f;
 #pragma unroll
-      for (int ww = hh * NWH; ww < (hh + 1) * NWH; ++ww) {
+      for (int j = 0; j < NWH; ++j) {
+        const int ww = hh * NWH + j;
         const float ew = fast_exp2(mm_s[ww][rr] - Mu);
         num += ew * mo[(ww * RT + rr) * DH + dh];
         den += ew * ml_s[ww][rr];
