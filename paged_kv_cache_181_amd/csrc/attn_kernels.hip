@@ -316,8 +316,10 @@ constexpr float kRescaleSlack = 8.f;
 // hw*NW/HP .. take head HP*blockIdx.y + hw, each group splitting the same
 // partition; a token row's HP heads (HP * 256 contiguous bytes at D = 128)
 // are then read together, and one workgroup runs per CU.
+// (The grouped forms run one workgroup per CU, so two waves per SIMD.)
 template <Fmt KV, Fmt QT, int D, int RT, bool PREFIX, int HP = 1>
-__global__ __launch_bounds__((Shape<KV, RT>::NW * kWave), (Shape<KV, RT>::WAVES_PER_SIMD))
+__global__ __launch_bounds__((Shape<KV, RT>::NW * kWave),
+                             (HP > 1 ? Shape<KV, RT>::NW / 4 : Shape<KV, RT>::WAVES_PER_SIMD))
 void attn_partition_kernel(const AttnArgs a) {
   using MM = Mma<QT>;
   using SM = AttnSmem<KV, D, RT>;
@@ -615,7 +617,7 @@ void attn_partition_kernel(const AttnArgs a) {
       };
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
-        if (t >= Q) break;                                   // wave-uniform
+        if (t >= Q) continue;                                // wave-uniform (no early exit, so the loop unrolls)
         float k[E], v[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) {
