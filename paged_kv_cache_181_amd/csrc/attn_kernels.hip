@@ -339,6 +339,12 @@ void attn_partition_kernel(const AttnArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int hw = w / NWH, wh = w % NWH;   // this wave's head within the workgroup, and its run
   const int rho = lane & 15, qd = lane >> 4;
+  // Lane rho is token rho of a loaded block and column rho of the score and
+  // output tiles.  In K8/V4 4-row tiles column rho computes query row rho % 4
+  // and carries the weights scaled by V group rho / 4, so one PV pass serves
+  // every group; elsewhere column rho is row rho (copies past the real rows).
+  constexpr bool COLG = KV == Fmt::K8V4 && RT == 4;
+  const int lrow = COLG ? (rho & 3) : rho;                  // the query row of column rho
   // (partition, KV head, sequence) of this workgroup.  K8/V4 runs on a 1-D
   // grid ordered so that every KV head of one (partition, sequence) lands on
   // the same XCD (workgroups go to the eight XCDs round-robin in dispatch
@@ -487,17 +493,17 @@ void attn_partition_kernel(const AttnArgs a) {
   const int w0 = b0 + wh * per;                             // first block of this wave's run
   const int nmine = max(0, min(per, be - w0));
 
-  // the query row this lane owns: rho = iq * G + hl, or in the prefix pass
-  // member rho / GQ's row (rho % GQ) (lanes past the rows compute a copy of
+  // the query row this lane owns: lrow = iq * G + hl, or in the prefix pass
+  // member lrow / GQ's row (lrow % GQ) (lanes past the rows compute a copy of
   // a real row; their results are never written)
   int row_len = L;                                          // the row's sequence length
-  bool row_ok = rho < GQT;
+  bool row_ok = lrow < GQT;
   if (PREFIX && row_ok) {
-    const int bm = a.grp_members[(int64_t)b * S + rho / GQ];
+    const int bm = a.grp_members[(int64_t)b * S + lrow / GQ];
     row_ok = bm >= 0;
     row_len = row_ok ? min(max(a.context_lens[bm], 0), a.max_blocks * kBlock) : 0;
   }
-  const int iq = row_ok ? (rho % GQ) / G : 0;
+  const int iq = row_ok ? (lrow % GQ) / G : 0;
   const int nvis = row_ok ? (row_len - Q + iq + 1) : L;     // visible positions of the row
   // every row sees j < full_lim (the prefix pass masks every tile instead)
   const int full_lim = PREFIX ? -(1 << 30) : L - Q + 1;
@@ -695,7 +701,7 @@ void attn_partition_kernel(const AttnArgs a) {
   }
   if constexpr (SM::QCOPIES == 1) __syncthreads();
   else wave_lds_fence();
-  const uint16_t* qrow = qw + (row_ok ? rho : rho % GQ) * QSTR;   // this lane's operand row
+  const uint16_t* qrow = qw + (row_ok ? lrow : lrow % GQ) * QSTR;   // this lane's operand row
   // start of every score accumulator: 0, or for K8/V4 -off * (the row's query
   // sum), which cancels the offset the converted K codes carry
   f4 s_init = f4{0.f, 0.f, 0.f, 0.f};
@@ -716,9 +722,10 @@ void attn_partition_kernel(const AttnArgs a) {
   f4 o[NT];
 #pragma unroll
   for (int n = 0; n < NT; ++n) o[n] = f4{0.f, 0.f, 0.f, 0.f};
-  float zacc[GR];
+  constexpr int NZ = COLG ? 1 : GR;     // zero-point sums: this column's group, or every group
+  float zacc[NZ];
 #pragma unroll
-  for (int gi = 0; gi < GR; ++gi) zacc[gi] = 0.f;
+  for (int gi = 0; gi < NZ; ++gi) zacc[gi] = 0.f;
 
   const float sl2 = a.scale_log2;
   const V4Consts v4c;                   // (used by K8/V4 only)
@@ -823,7 +830,7 @@ void attn_partition_kernel(const AttnArgs a) {
       for (int n = 0; n < NT; ++n) o[n] *= alpha;
       l_run *= alpha;
 #pragma unroll
-      for (int gi = 0; gi < GR; ++gi) zacc[gi] *= alpha;
+      for (int gi = 0; gi < NZ; ++gi) zacc[gi] *= alpha;
       m_run = m_new;
     }
     const float m_use = m_run == kNegInf ? 0.f : m_run;
@@ -833,7 +840,27 @@ void attn_partition_kernel(const AttnArgs a) {
     l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 
     // ---- O^T += V^T P^T; the V operand comes from one transposing read per tile
-    if constexpr (KV == Fmt::K8V4) {
+    if constexpr (COLG) {
+      // this column's group (columns past the groups compute a copy)
+      const int gl = min(rho >> 2, GR - 1);
+      float pw[4];
+      float zs = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float* sd = side + 16 + (4 * qd + r) * 2 * GR + 2 * gl;
+        pw[r] = pr[r] * sd[0];
+        zs += pr[r] * sd[1];
+      }
+      zacc[0] += zs;
+      u2 phi, plo;
+      Mma<Fmt::F16>::split(pw, phi, plo);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const u2 av = lds_read_tr16(vst + tr_off + (n >> 1) * 1024 + (n & 1) * 512);
+        o[n] = Mma<Fmt::F16>::pv(av, phi, o[n]);
+        o[n] = Mma<Fmt::F16>::pv(av, plo, o[n]);
+      }
+    } else if constexpr (KV == Fmt::K8V4) {
 #pragma unroll
       for (int gi = 0; gi < GR; ++gi) {
         float pw[4];
@@ -903,9 +930,9 @@ void attn_partition_kernel(const AttnArgs a) {
   l_run = quarter_sum(l_run);
   if constexpr (KV == Fmt::K8V4) {
 #pragma unroll
-    for (int gi = 0; gi < GR; ++gi) zacc[gi] = quarter_sum(zacc[gi]);
+    for (int gi = 0; gi < NZ; ++gi) zacc[gi] = quarter_sum(zacc[gi]);
 #pragma unroll
-    for (int n = 0; n < NT; ++n) o[n] += zacc[n / 2];
+    for (int n = 0; n < NT; ++n) o[n] += zacc[COLG ? 0 : n / 2];
   }
 
   // ---- merge the NW wavefronts of this workgroup (LDS reused), in EP passes
@@ -920,7 +947,18 @@ void attn_partition_kernel(const AttnArgs a) {
 #pragma unroll
   for (int e = 0; e < EP; ++e) {
     __syncthreads();                           // the block loop's, or the last pass's, reads done
-    if (rho < RT && rho < GQT) {
+    if constexpr (COLG) {
+      // row lrow's dims of tile n sit in the columns of tile n's V group
+      if (lrow < GQT) {
+#pragma unroll
+        for (int n = 0; n < NTH; ++n) {
+          if ((rho >> 2) != (e * NTH + n) / 2) continue;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            mo[(w * RT + lrow) * DH + 16 * n + v4_dim(4 * qd + r)] = o[e * NTH + n][r];
+        }
+      }
+    } else if (rho < RT && rho < GQT) {
 #pragma unroll
       for (int n = 0; n < NTH; ++n)
 #pragma unroll
