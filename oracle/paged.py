@@ -33,8 +33,11 @@ Sources (page title, then the part of it used):
 Readings where the pages are silent are listed next to each function.
 
 Parity status: every function here is pinned by ``tests/test_oracle_pins.py``
-(brute force, closed forms, invariants, hand-built quantizer vectors); none is
-"parity unpinned".
+against something other than itself (brute force through independent code
+paths, closed forms, invariants, hand-built quantizer vectors, K8/V4 side
+arrays checked slot by slot against the input rows, the length clamp against
+attention at the table's capacity), and a planted mistake in each of these
+parts fails a pin.
 """
 
 from __future__ import annotations
@@ -64,19 +67,6 @@ def decode(bits: np.ndarray, fmt: str) -> np.ndarray:
         return bits.view(np.float16).astype(np.float64)
     if fmt == FMT_BF16:
         return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
-    raise ValueError(f"unknown 16-bit format {fmt!r}")
-
-
-def encode_f64(values: np.ndarray, fmt: str) -> np.ndarray:
-    """float64 -> stored bits with round-to-nearest-even (used for output casts)."""
-    v = np.asarray(values, dtype=np.float64)
-    if fmt == FMT_F16:
-        return v.astype(np.float16).view(np.uint16)
-    if fmt == FMT_BF16:
-        f32 = v.astype(np.float32)
-        u = f32.view(np.uint32).astype(np.uint64)
-        rnd = ((u >> np.uint64(16)) & np.uint64(1)) + np.uint64(0x7FFF)
-        return ((u + rnd) >> np.uint64(16)).astype(np.uint16)
     raise ValueError(f"unknown 16-bit format {fmt!r}")
 
 

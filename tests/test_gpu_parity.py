@@ -1126,8 +1126,18 @@ def _peaked(case, factor=4.0):
     """The same case with the queries multiplied by `factor` (exact in fp16:
     a power of two), which sharpens every softmax row."""
     import dataclasses
-    qf = oracle.decode(case.query, case.fmt) * factor
-    return dataclasses.replace(case, query=oracle.encode_f64(qf, case.fmt))
+    bits = case.query
+    if case.fmt == "f16":
+        scaled = (bits.view(np.float16).astype(np.float32) * np.float32(factor)).astype(np.float16)
+        out = scaled.view(np.uint16)
+    else:
+        f = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32) * np.float32(factor)
+        u = f.view(np.uint32)
+        assert not (u & 0xFFFF).any()                 # a power-of-two factor is exact
+        out = (u >> np.uint32(16)).astype(np.uint16)
+    # exact: scaling back recovers every query value
+    assert np.array_equal(oracle.decode(out, case.fmt) / factor, oracle.decode(bits, case.fmt))
+    return dataclasses.replace(case, query=out)
 
 
 @pytest.mark.parametrize("name,factor,tau", [

@@ -573,6 +573,116 @@ def test_k8v4_write_and_attention_use_the_same_codes():
         np.testing.assert_allclose(out[b], o[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
 
 
+def _k8v4_write_errors(write):
+    """Checks one K8/V4 write against the input rows, not against the oracle's
+    own dequantization: distinct rows go to scattered slots (some skipped), and
+    at each written slot the side arrays must sit at [block, row, head(, group)]
+    and decode, by this test's own arithmetic, to within half a step of that
+    slot's input row; a hand row fixes one scale and one zero exactly.
+    Returns the list of failures (empty when the write is right)."""
+    errors = []
+    rng = np.random.default_rng(77)
+    nb, hkv, d = 6, 2, 64
+    T = 9
+    key = rng.standard_normal((T, hkv, d)).astype(np.float16)
+    value = (rng.standard_normal((T, hkv, d)) * 2 + 0.5).astype(np.float16)
+    # hand row (token 0, head 1): K amax 127/4 -> scale 0.25; V group 0 spans
+    # 3 .. 3 + 15/2 -> scale 0.5, zero 3; group 1 spans -2 .. -2 + 15/4 ->
+    # scale 0.25, zero -2 (scale and zero differ in both groups)
+    key[0, 1] = 0
+    key[0, 1, 5] = np.float16(127 / 4)
+    key[0, 1, 6] = np.float16(-1.0)                # code -4 exactly
+    value[0, 1, :32] = (3 + 0.5 * (np.arange(32) % 16)).astype(np.float16)
+    value[0, 1, 32:] = (-2 + 0.25 * (np.arange(32) % 16)).astype(np.float16)
+    slots = np.array([37, 3, -1, 90, 16, 95, nb * 16 + 4, 50, 64], np.int64)
+    kbits = key.view(np.uint16)
+    vbits = value.view(np.uint16)
+    sentinel = (np.full((nb, 16, hkv, d), 99, np.int8), np.full((nb, 16, hkv), 9, np.float16),
+                np.full((nb, 16, hkv, d // 2), 0xAB, np.uint8),
+                np.full((nb, 16, hkv, d // 32), 9, np.float16),
+                np.full((nb, 16, hkv, d // 32), 9, np.float16))
+    kq, ks, vq, vs, vz = write(kbits, vbits, "f16", *sentinel, slots)
+    written = set()
+    for t, s in enumerate(slots.tolist()):
+        if s < 0 or s >= nb * 16:
+            continue
+        blk, off = divmod(s, 16)
+        written.add((blk, off))
+        for h in range(hkv):
+            k = key[t, h].astype(np.float64)
+            v = value[t, h].astype(np.float64)
+            sk = float(ks[blk, off, h])
+            khat = kq[blk, off, h].astype(np.float64) * sk
+            if sk <= 0 or np.abs(khat - k).max() > sk / 2 * (1 + 2**-10) + 1e-12:
+                errors.append(f"K of token {t} head {h} at slot {s}")
+            codes = np.empty(d)
+            codes[0::2] = vq[blk, off, h] & 0xF
+            codes[1::2] = vq[blk, off, h] >> 4
+            for gi in range(d // 32):
+                sv, zv = float(vs[blk, off, h, gi]), float(vz[blk, off, h, gi])
+                vhat = codes[32 * gi:32 * gi + 32] * sv + zv
+                vin = v[32 * gi:32 * gi + 32]
+                if np.abs(vhat - vin).max() > sv / 2 * (1 + 2**-9) + 1e-12:
+                    errors.append(f"V group {gi} of token {t} head {h} at slot {s}")
+    hb, ho = divmod(int(slots[0]), 16)
+    if float(ks[hb, ho, 1]) != 0.25 or int(kq[hb, ho, 1, 5]) != 127 or int(kq[hb, ho, 1, 6]) != -4:
+        errors.append("hand K row")
+    if (float(vs[hb, ho, 1, 0]), float(vz[hb, ho, 1, 0])) != (0.5, 3.0):
+        errors.append("hand V group 0 scale/zero")
+    if (float(vs[hb, ho, 1, 1]), float(vz[hb, ho, 1, 1])) != (0.25, -2.0):
+        errors.append("hand V group 1 scale/zero")
+    if list(vq[hb, ho, 1, :8]) != [0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE]:
+        errors.append("hand V codes")
+    # nothing else changed
+    for blk in range(nb):
+        for off in range(16):
+            if (blk, off) in written:
+                continue
+            if not (np.all(kq[blk, off] == 99) and np.all(ks[blk, off] == 9) and
+                    np.all(vq[blk, off] == 0xAB) and np.all(vs[blk, off] == 9) and
+                    np.all(vz[blk, off] == 9)):
+                errors.append(f"slot {blk * 16 + off} changed")
+    return errors
+
+
+def test_k8v4_write_places_each_row_at_its_slot():
+    assert _k8v4_write_errors(oracle.kv_cache_write_k8v4) == []
+
+
+def test_planted_k8v4_side_array_mistakes_are_caught():
+    def swapped(*args):
+        kq, ks, vq, vs, vz = oracle.kv_cache_write_k8v4(*args)
+        return kq, ks, vq, vz, vs                   # V scale and zero exchanged
+    assert _k8v4_write_errors(swapped)
+
+    def wrong_row(key, value, fmt, *arrs_and_slots):
+        *arrs, slots = arrs_and_slots
+        return oracle.kv_cache_write_k8v4(key, value, fmt, *arrs, slots ^ 1)   # row off by one
+    assert _k8v4_write_errors(wrong_row)
+
+    def wrong_head(key, value, fmt, *rest):
+        return oracle.kv_cache_write_k8v4(key[:, ::-1], value[:, ::-1], fmt, *rest)
+    assert _k8v4_write_errors(wrong_head)
+
+
+def test_length_is_clamped_to_the_table_capacity():
+    # a length past max_blocks * 16 reads the whole table and nothing more
+    # (the table has exactly the capacity's worth of valid entries), and a
+    # negative length sees nothing
+    case = small_case(34, batch=2, q_len=2, lengths=[5, 17])
+    cap = case.max_blocks * 16
+    case.context_lens[:] = cap
+    case.block_tables[:] = np.arange(case.max_blocks * 2, dtype=np.int32).reshape(2, -1) % \
+        case.num_blocks
+    ref = sdpa_reference(case)
+    case.context_lens[:] = [cap + 37, cap + 1]
+    np.testing.assert_allclose(run_oracle(case), ref, rtol=0, atol=1e-12)
+    assert oracle.effective_length(cap + 37, case.max_blocks) == cap
+    case.context_lens[:] = [-3, 0]
+    out = run_oracle(case)
+    assert not out.any()
+
+
 # ---------------------------------------------------------------------------
 # 5. the generators produce the declared structure
 # ---------------------------------------------------------------------------
