@@ -115,8 +115,6 @@ def test_kv_cache_write_empty_is_noop(P):
 @pytest.mark.parametrize("split,psize", [(False, 0), (True, 512), (True, 32)])
 def test_decode_matches_oracle(P, name, split, psize):
     case, ref = get_case(name)
-    if case.name == "long32k" and not split:
-        pytest.skip("the 32K single sequence is a split-KV workload")
     dc = DevCase(case)
     out32 = run_decode(P, dc, split=split, partition_size=psize or 512)
     err = max_err(out32, ref)
@@ -465,8 +463,6 @@ def run_append(P, dc, *, split, psize=512, out_dtype=torch.float32, bt=None, mcl
 @pytest.mark.parametrize("split,psize", [(False, 0), (True, 512), (True, 32)])
 def test_append_matches_write_then_attend(P, name, split, psize):
     case, (ref, kc, vc) = get_append_case(name)
-    if case.name == "long32k" and not split:
-        pytest.skip("the 32K single sequence is a split-KV workload")
     dc = DevCase(case)
     out, k, v = run_append(P, dc, split=split, psize=psize or 512)
     assert np.array_equal(dev_to_bits(k), kc), "key cache after the append differs"
@@ -828,8 +824,6 @@ def run_window(P, dc, window, *, split, psize=512, out_dtype=torch.float32, k=No
 @pytest.mark.parametrize("split,psize", [(False, 0), (True, 512), (True, 32)])
 def test_window_matches_oracle(P, name, window, split, psize):
     case, _ = get_case(name)
-    if case.name == "long32k" and not split:
-        pytest.skip("the 32K single sequence is a split-KV workload")
     ref = window_ref(name, window)
     dc = DevCase(case)
     out = run_window(P, dc, window, split=split, psize=psize or 512)
@@ -885,8 +879,6 @@ def run_window_append(P, dc, window, *, split, psize=512, out_dtype=torch.float3
 @pytest.mark.parametrize("split,psize", [(False, 0), (True, 512), (True, 32)])
 def test_window_append_matches_write_then_windowed_attend(P, name, window, split, psize):
     case, _ = get_case(name)
-    if case.name == "long32k" and not split:
-        pytest.skip("the 32K single sequence is a split-KV workload")
     ref, kc, vc = window_append_ref(name, window)
     dc = DevCase(case)
     out, k, v = run_window_append(P, dc, window, split=split, psize=psize or 512)
