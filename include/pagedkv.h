@@ -172,6 +172,35 @@ int paged_attention_decode_splitkv(void* out, int out_dtype, const void* query,
                                    void* stream);
 
 /*
+ * paged_attention_decode_splitkv_noalloc — paged_attention_decode_splitkv for
+ * callers that cannot allocate memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the same arguments without
+ * the workspace, the same kernels and the same result bit for bit.  The
+ * partials go to a static device array of PKV_NOALLOC_SCRATCH_BYTES bytes
+ * inside the library, one per GPU (each GPU holds it until the process ends);
+ * its device address is looked up on the first call on each device, and no
+ * call allocates or frees anything.
+ *   - A call whose partials need more than PKV_NOALLOC_SCRATCH_BYTES
+ *     (batch * q_len * num_q_heads * ceil(max_context_len / partition_size)
+ *     * (head_dim + 2) * 4 bytes) returns PKV_ERR_WORKSPACE and launches
+ *     nothing.
+ *   - Every call on one GPU shares that GPU's array: two calls that overlap in
+ *     time on one GPU (different streams, or different threads) race and
+ *     produce garbage.  Calls in stream order on one stream are safe.  The
+ *     array keeps the last call's partials; nothing needs to start at zero.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (16u * 1024u * 1024u)
+
+int paged_attention_decode_splitkv_noalloc(void* out, int out_dtype, const void* query,
+                                           const void* key_cache, const void* value_cache,
+                                           int kv_dtype, const int32_t* block_tables,
+                                           int max_blocks_per_seq, const int32_t* context_lens,
+                                           int batch, int q_len, int num_q_heads, int gqa_factor,
+                                           int head_dim, int block_size, int64_t num_blocks,
+                                           float scale, int max_context_len, int partition_size,
+                                           void* stream);
+
+/*
  * The two halves of paged_attention_decode_splitkv as separate launches, for
  * callers that schedule or combine them themselves (e.g. to merge partials of
  * several passes).

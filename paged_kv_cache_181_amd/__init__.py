@@ -23,7 +23,8 @@ _EXPORTS = (
     "paged_attention_decode_cascade", "cascade_workspace_size",
     "paged_attention_decode_splitkv_sparse_v", "paged_attention_decode_k8v4_append",
     "paged_attention_decode_splitkv_k8v4_append", "paged_attention_decode_window_append",
-    "paged_attention_decode_splitkv_window_append",
+    "paged_attention_decode_splitkv_window_append", "paged_attention_decode_splitkv_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
 )
 
 __all__ = list(_EXPORTS)

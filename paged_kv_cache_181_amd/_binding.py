@@ -58,6 +58,7 @@ SIGNATURES = {
     "paged_attention_decode_splitkv_workspace_size": ([_i, _i, _i, _i, _i, _i,
                                                        ctypes.POINTER(_sz)], _i),
     "paged_attention_decode_splitkv": (_ATTN + [_i, _i, _p, _sz, _p], _i),
+    "paged_attention_decode_splitkv_noalloc": (_ATTN + [_i, _i, _p], _i),
     "kv_cache_write_k8v4": ([_p, _p, _i, _p, _p, _p, _p, _p, _p, _i64, _i, _i, _i, _i64, _p], _i),
     "paged_attention_decode_k8v4": (_ATTN_K8V4 + [_p], _i),
     "paged_attention_decode_splitkv_k8v4": (_ATTN_K8V4 + [_i, _i, _p, _sz, _p], _i),
@@ -237,6 +238,27 @@ def paged_attention_decode_splitkv(out, query, key_cache, value_cache, block_tab
         _dtype_code(key_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
         B, Q, Hq, gqa_factor, D, key_cache.shape[1], key_cache.shape[0], float(scale),
         int(max_context_len), int(partition_size), _ptr(workspace), nbytes, _stream(dev)))
+
+
+NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024     # PKV_NOALLOC_SCRATCH_BYTES
+
+
+def paged_attention_decode_splitkv_noalloc(out, query, key_cache, value_cache, block_tables,
+                                           context_lens, scale, gqa_factor, max_context_len,
+                                           partition_size):
+    """Split-KV decode with the partials in the library's static per-GPU
+    scratch (no workspace argument, nothing allocated); calls that overlap in
+    time on one GPU race."""
+    dev = _dev(out, query, key_cache, value_cache, block_tables, context_lens)
+    B, Q, Hq, D = _attn_common(out, query, block_tables, context_lens, gqa_factor)
+    _expect(key_cache.shape == value_cache.shape and key_cache.shape[2:] == (Hq // gqa_factor, D),
+            "caches must be [NB, 16, Hq/G, D]")
+    _expect(query.dtype == key_cache.dtype == value_cache.dtype, "query/cache dtype mismatch")
+    _check(lib.paged_attention_decode_splitkv_noalloc(
+        _ptr(out), _dtype_code(out), _ptr(query), _ptr(key_cache), _ptr(value_cache),
+        _dtype_code(key_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        B, Q, Hq, gqa_factor, D, key_cache.shape[1], key_cache.shape[0], float(scale),
+        int(max_context_len), int(partition_size), _stream(dev)))
 
 
 def _append_args(out, query, new_key, new_value, key_cache, value_cache, block_tables,

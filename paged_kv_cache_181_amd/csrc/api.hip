@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "../../include/pagedkv.h"
 #include "pkv_common.h"
@@ -143,6 +144,34 @@ int check_k8v4_pointers(const void* k_scale, const void* v_scale, const void* v_
   if ((reinterpret_cast<uintptr_t>(k_scale) & 1u) || (reinterpret_cast<uintptr_t>(v_scale) & 7u) ||
       (reinterpret_cast<uintptr_t>(v_zero) & 7u))
     return fail(PKV_ERR_ALIGN, "k_scale must be 2-byte and v_scale/v_zero 8-byte aligned");
+  return PKV_OK;
+}
+
+// Split-KV partials of paged_attention_decode_splitkv_noalloc: one static
+// device array per GPU the library runs on, held until the process ends.  Its
+// name is only a host-side handle; kernels get its device address, looked up
+// once per device (with that device current) and kept per device.
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PKV_ERR_LAUNCH, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PKV_ERR_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(PKV_ERR_LAUNCH, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return PKV_OK;
 }
 
@@ -293,6 +322,41 @@ int paged_attention_decode_splitkv(void* out, int out_dtype, const void* query,
   if (rc) return rc;
   return launch_result(pkv::launch_attention(a, kv_dtype, kv_dtype, head_dim, (hipStream_t)stream),
                        "paged_attention_decode_splitkv");
+}
+
+int paged_attention_decode_splitkv_noalloc(void* out, int out_dtype, const void* query,
+                                           const void* key_cache, const void* value_cache,
+                                           int kv_dtype, const int32_t* block_tables,
+                                           int max_blocks_per_seq, const int32_t* context_lens,
+                                           int batch, int q_len, int num_q_heads, int gqa_factor,
+                                           int head_dim, int block_size, int64_t num_blocks,
+                                           float scale, int max_context_len, int partition_size,
+                                           void* stream) {
+  if (kv_dtype != PKV_F16 && kv_dtype != PKV_BF16)
+    return fail(PKV_ERR_UNSUPPORTED, "kv_dtype must be PKV_F16 or PKV_BF16");
+  pkv::AttnArgs a{};
+  int rc = check_attention(out, out_dtype, query, key_cache, value_cache, block_tables,
+                           max_blocks_per_seq, context_lens, batch, q_len, num_q_heads, gqa_factor,
+                           head_dim, block_size, num_blocks, scale, a);
+  if (rc) return rc;
+  if (batch == 0) return ok();
+  int64_t parts = 0;
+  size_t need = 0;
+  rc = split_geometry(batch, q_len, num_q_heads, head_dim, max_context_len, partition_size, parts,
+                      need);
+  if (rc) return rc;
+  if (need > (size_t)PKV_NOALLOC_SCRATCH_BYTES)
+    return fail(PKV_ERR_WORKSPACE,
+                "the partials need %zu bytes, more than the %zu-byte static scratch holds "
+                "(use paged_attention_decode_splitkv with a workspace)",
+                need, (size_t)PKV_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc) return rc;
+  rc = setup_split(a, head_dim, max_context_len, partition_size, ws, PKV_NOALLOC_SCRATCH_BYTES);
+  if (rc) return rc;
+  return launch_result(pkv::launch_attention(a, kv_dtype, kv_dtype, head_dim, (hipStream_t)stream),
+                       "paged_attention_decode_splitkv_noalloc");
 }
 
 int paged_attention_decode_window(void* out, int out_dtype, const void* query,
