@@ -19,6 +19,7 @@ resident in HBM.  The dominant kernel's roofline entry uses HIP events around
 second pass of the same work (the headline pass carries no extra events).
 
 python bench.py [--steps K] [--warmup W] [--no-extra] [--no-cpu-baseline]
+python bench.py --ceiling      # read ceiling of the 32K layer (probe library) + the kernel
 """
 
 from __future__ import annotations
@@ -53,6 +54,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (scale for rocprofv3 byte counters)")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="only measure the read ceiling of the 32K layer with the probe library, "
+                         "next to the partition kernel")
     ap.add_argument("--only", default=None,
                     help="time only this one of the other workloads (for profiling), e.g. k8v4")
     return ap.parse_args()
@@ -128,6 +132,13 @@ class Long32K:
                                              self.cl, c.scale, c.gqa_factor, self.L,
                                              self.partition, self.ws)
 
+    def step_write_only(self):
+        """Only the slot scatter of a step: one kv_cache_write per layer (the
+        new token's K and V rows into that layer's cache)."""
+        P = self.P
+        for l in range(self.layers):
+            P.kv_cache_write(self.nk[l], self.nv[l], self.K[l], self.V[l], self.slots)
+
     def step_timed_kernels(self):
         """The same work as a step, reordered so that the 32 partition-kernel
         launches run back to back between two events: the partition kernels
@@ -164,17 +175,26 @@ def graph_of(torch, fn):
     return g
 
 
-def time_steps(torch, fn, steps, warmup):
+def time_steps(torch, fn, steps, warmup, median=False):
+    """ms per step over `steps` steps after `warmup` untimed ones: the mean
+    (first to last event), and with `median` also the median of the per-step
+    intervals (an event between consecutive steps)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
         fn()
-    e.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return s.elapsed_time(e) / steps          # ms per step
+    mean = ev[0].elapsed_time(ev[-1]) / steps
+    if not median:
+        return mean
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    mid = steps // 2
+    med = per[mid] if steps % 2 else 0.5 * (per[mid - 1] + per[mid])
+    return mean, med
 
 
 def kernel_average_ms(torch, wl, steps):
@@ -274,9 +294,9 @@ OTHER = {
     # partition is the caller's choice for these batches: the fastest of a
     # sweep over direct, 256, 512, 1024 and 2048 on MI355X
     "tiny": (1, 32, 0),
-    "llama8b_batch": (2, 8, 2048),
-    "spec_verify": (4, 8, 1024),
-    "k8v4": (5, 8, 2048),
+    "llama8b_batch": (2, 32, 2048),
+    "spec_verify": (4, 32, 1024),
+    "k8v4": (5, 32, 2048),
     "long32k_window2048": (3, 32, 128),
 }
 WINDOW = {"long32k_window2048": 2048}       # sliding window of the windowed workloads
@@ -362,8 +382,8 @@ def other_workload(name, P, W, torch, steps, warmup):
                 else:
                     P.paged_attention_decode_append(out[l], q[l], nk[l], nv[l], K[l], V[l], bt,
                                                     cl, scale, G)
-    ms = time_steps(torch, graph_of(torch, step).replay, steps, warmup)
-    extra = {}
+    ms, med = time_steps(torch, graph_of(torch, step).replay, steps, warmup, median=True)
+    extra = {"median_us_per_layer": round(med * 1e3 / layers, 3)}
     if name == "k8v4" or window:
         ms2 = time_steps(torch, graph_of(torch, step_two_call).replay, steps, warmup)
         extra["two_call_us_per_layer"] = round(ms2 * 1e3 / layers, 3)
@@ -518,6 +538,102 @@ def sparse_v_workload(P, W, torch, steps, warmup, layers=32, tau=1e-3, sharpen=8
                     "split-KV on the same inputs, partition 512, HIP graph"}
 
 
+# ----------------------------------------------------------------------------
+# Streaming ceiling of the 32K layer (--ceiling): how fast the same 32 x 128 MiB
+# can be read at all, by read-only probes (libpagedkv_probe.so) timed exactly
+# like the partition kernel (HIP events around 32 back-to-back launches, one
+# per layer cache), next to the partition kernel itself.
+
+# (label, heads per workgroup, waves, blocks per partition, depth, LDS bytes)
+PAGED_SHAPES = [
+    ("one head per workgroup, 8 waves x 4 blocks, 2 workgroups per CU (one-head kernel's shape)",
+     1, 8, 32, 2, 60 * 1024),
+    ("head pairs, 8 waves x 8 blocks, 1 workgroup per CU (the shipped kernel's shape)",
+     2, 8, 32, 2, 82 * 1024),
+    ("head pairs, depth 3", 2, 8, 32, 3, 82 * 1024),
+    ("head pairs, depth 4", 2, 8, 32, 4, 82 * 1024),
+    ("head pairs, 16 waves x 4 blocks, depth 3", 2, 16, 32, 3, 82 * 1024),
+    ("head quads, 8 waves x 8 blocks, 256-token partitions", 4, 8, 16, 2, 82 * 1024),
+    ("head quads, depth 4", 4, 8, 16, 4, 82 * 1024),
+    ("all 8 heads, 8 waves x 8 blocks, 128-token partitions", 8, 8, 8, 2, 82 * 1024),
+    ("all 8 heads, depth 4", 8, 8, 8, 4, 82 * 1024),
+    ("all 8 heads, 16 waves x 4 blocks, depth 3", 8, 16, 8, 3, 82 * 1024),
+]
+# (workgroups, waves, depth)
+STREAM_SHAPES = [(256, 8, 4), (256, 16, 4), (512, 8, 2), (512, 8, 4), (1024, 8, 2), (1024, 4, 4),
+                 (2048, 4, 2), (2048, 8, 1)]
+
+
+def ceiling_mode(P, W, torch, args):
+    import statistics
+    from paged_kv_cache_181_amd import probe
+    log("building the 32K workload")
+    wl = Long32K(P, W, torch, args.layers, args.partition, args.seed)
+    dev = torch.device("cuda:0")
+    sink = torch.zeros(1 << 16, dtype=torch.float32, device=dev)
+    reps = max(args.steps, 5)
+
+    def timed(launch):
+        """median over `reps` of the per-launch time of 32 back-to-back launches"""
+        for l in range(wl.layers):          # warm-up pass
+            launch(l)
+        torch.cuda.synchronize()
+        per = []
+        for _ in range(reps):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for l in range(wl.layers):
+                launch(l)
+            e.record()
+            torch.cuda.synchronize()
+            per.append(s.elapsed_time(e) * 1e3 / wl.layers)
+        return statistics.median(per), min(per), max(per)
+
+    def row(us, lo, hi, **kw):
+        return {**kw, "us_per_launch": round(us, 3), "us_min": round(lo, 3), "us_max": round(hi, 3),
+                "tb_per_s": round(wl.layer_bytes / (us * 1e-6) / 1e12, 3),
+                "pct_of_hbm_peak": round(100 * wl.layer_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
+
+    out = {"workload": "long32k layer caches (32 x 128 MiB of K and V, fp16)",
+           "bytes_per_launch": wl.layer_bytes, "launches_per_timing": wl.layers,
+           "timings": reps, "stream": [], "paged": []}
+    for wgs, waves, depth in STREAM_SHAPES:
+        log(f"stream read {wgs} x {waves} waves, depth {depth}")
+        r = timed(lambda l: probe.stream_read(wl.K[l], wl.V[l], wgs, waves, depth, sink))
+        out["stream"].append(row(*r, workgroups=wgs, waves=waves, depth=depth))
+    for label, hp, waves, part, depth, lds in PAGED_SHAPES:
+        log(f"paged read: {label}")
+        r = timed(lambda l: probe.paged_read(wl.K[l], wl.V[l], wl.bt, hp, waves, part, depth, lds,
+                                             sink))
+        out["paged"].append(row(*r, shape=label, heads_per_workgroup=hp, waves=waves,
+                                blocks_per_partition=part, depth=depth))
+    c = wl.case
+    log("partition kernel (append form, as the headline step)")
+    if not hasattr(wl, "wss"):
+        wl.wss = [torch.zeros_like(wl.ws) for _ in range(wl.layers)]
+    r = timed(lambda l: P.paged_attention_decode_splitkv_append_partials(
+        wl.q[l], wl.nk[l], wl.nv[l], wl.K[l], wl.V[l], wl.bt, wl.cl, c.scale, c.gqa_factor, wl.L,
+        wl.partition, wl.wss[l]))
+    out["partition_kernel"] = row(*r, kernel="attn_partition_kernel<F16,F16,128,4> head-pair form")
+    r = timed(lambda l: P.paged_attention_decode_splitkv_merge(wl.out[l], wl.L, wl.partition,
+                                                                wl.wss[l]))
+    out["merge_kernel_us_per_launch"] = round(r[0], 3)
+    best_stream = min(out["stream"], key=lambda x: x["us_per_launch"])
+    best_paged = min(out["paged"], key=lambda x: x["us_per_launch"])
+    shipped = out["paged"][1]
+    k_us = out["partition_kernel"]["us_per_launch"]
+    out["summary"] = {
+        "best_stream_us": best_stream["us_per_launch"],
+        "best_paged_us": best_paged["us_per_launch"], "best_paged_shape": best_paged["shape"],
+        "shipped_shape_read_us": shipped["us_per_launch"],
+        "partition_kernel_us": k_us,
+        "kernel_frac_of_best_stream": round(best_stream["us_per_launch"] / k_us, 4),
+        "kernel_frac_of_shipped_shape_read": round(shipped["us_per_launch"] / k_us, 4),
+        "us_per_layer_at_70pct_of_peak": round(wl.layer_bytes / (0.7 * HBM_PEAK_GBS * 1e9) * 1e6, 3),
+    }
+    print(json.dumps({"ceiling": out}), flush=True)
+
+
 def copy_calibration(torch):
     """A plain device copy of known size: 1 GiB read + 1 GiB written per launch.
     rocprofv3's FETCH_SIZE / WRITE_SIZE for these launches give the scale
@@ -547,6 +663,9 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch)
         return
+    if args.ceiling:
+        ceiling_mode(P, W, torch, args)
+        return
     if args.only:
         runners = {n: (lambda n=n: other_workload(n, P, W, torch, args.steps, args.warmup))
                    for n in OTHER}
@@ -568,11 +687,14 @@ def main():
     log("timing steps")
     eager_ms = time_steps(torch, wl.step, args.steps, args.warmup)
     graph = graph_of(torch, wl.step)
-    ms = time_steps(torch, graph.replay, args.steps, args.warmup)
+    ms, med_ms = time_steps(torch, graph.replay, args.steps, args.warmup, median=True)
     two_call_ms = time_steps(torch, graph_of(torch, wl.step_two_call).replay, args.steps,
                              args.warmup)
+    write_ms = time_steps(torch, graph_of(torch, wl.step_write_only).replay, args.steps,
+                          args.warmup)
     gbs = wl.step_bytes / (ms * 1e-3) / 1e9
-    log(f"{ms:.3f} ms/step ({eager_ms:.3f} eager, {two_call_ms:.3f} two-call), {gbs:.1f} GB/s")
+    log(f"{ms:.3f} ms/step (median {med_ms:.3f}; {eager_ms:.3f} eager, {two_call_ms:.3f} two-call, "
+        f"{write_ms:.3f} the writes alone), {gbs:.1f} GB/s")
     kern_ms, launches = kernel_average_ms(torch, wl, args.steps)
     achieved = wl.layer_bytes / (kern_ms * 1e-3) / 1e9
     log(f"partition kernel {kern_ms * 1e3:.2f} us avg over {launches} launches, {achieved:.1f} GB/s")
@@ -601,8 +723,13 @@ def main():
         },
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "us_per_layer": round(ms * 1e3 / args.layers, 3),
+        "median_ms_per_step": round(med_ms, 4),
+        "median_us_per_layer": round(med_ms * 1e3 / args.layers, 3),
+        "median_pct_of_hbm_peak": round(100 * wl.step_bytes / (med_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                        2),
         "eager_ms_per_step": round(eager_ms, 4),
         "two_call_ms_per_step": round(two_call_ms, 4),
+        "kv_cache_write_us_per_layer": round(write_ms * 1e3 / args.layers, 3),
         "decode_tokens_per_s": round(1e3 / ms, 2),
         "roofline": {
             "bound": "hbm",

@@ -19,6 +19,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpagedkv.so")
 SOURCES = ["api.hip", "write_kernels.hip", "attn_kernels.hip", "gather_kernels.hip"]
+# read-only measurement probes (pagedkv_probe.h), a library of their own
+PROBE_LIB = os.path.join(PKG, "libpagedkv_probe.so")
+PROBE_SOURCES = ["probe_kernels.hip"]
 ARCH = "gfx950"
 
 
@@ -36,13 +39,20 @@ def flags():
 
 
 def build(verbose: bool = False, jobs: int = 4) -> str:
-    """Compile every source (always, even if the library exists) and link."""
+    """Compile every source (always, even if the libraries exist) and link the
+    decode library and the probe library."""
+    _build_lib(SOURCES, LIB, verbose, jobs)
+    _build_lib(PROBE_SOURCES, PROBE_LIB, verbose, jobs)
+    return LIB
+
+
+def _build_lib(sources, lib, verbose, jobs):
     cc = hipcc()
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
     procs = []
     objs = []
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         objs.append(obj)
         cmd = [cc, *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
@@ -53,15 +63,14 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
             _wait(procs.pop(0))
     while procs:
         _wait(procs.pop(0))
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     out = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if out.returncode != 0:
         raise RuntimeError("link failed:\n" + out.stdout)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 def _wait(item):

@@ -29,8 +29,8 @@ def P():
     return lib
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
                        text, flags=re.M)
@@ -55,6 +55,53 @@ def test_library_exports_every_declared_symbol(P):
 def test_binding_covers_every_declared_symbol(P):
     from paged_kv_cache_181_amd import _binding
     assert set(declared_functions()) <= set(_binding.SIGNATURES)
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "pagedkv_probe.h")
+
+
+def test_probe_library_exports_and_binds_every_declared_symbol(P):
+    from paged_kv_cache_181_amd import probe
+    names = declared_functions(PROBE_HEADER)
+    assert {"pkv_probe_stream_read", "pkv_probe_paged_read", "pkv_probe_last_error"} <= set(names)
+    raw = ctypes.CDLL(probe.LIB_PATH)
+    for name in names:
+        assert hasattr(raw, name), name
+    assert set(names) <= set(probe.SIGNATURES)
+
+
+@pytest.mark.parametrize("args,code", [
+    # buf0, buf1, bytes_each, workgroups, waves, depth, sink, sink_count
+    ((0, 16, 1 << 20, 2, 8, 2, 16, 64), -1),           # NULL buffer
+    ((16, 16, 1 << 20, 2, 6, 2, 16, 64), -3),          # waves not 4, 8 or 16
+    ((16, 16, 1 << 20, 2, 8, 3, 16, 64), -3),          # depth 3
+    ((16, 16, 1 << 20, 3, 8, 2, 16, 64), -2),          # odd workgroup count
+    ((16, 16, 1000, 2, 8, 2, 16, 64), -2),             # not a whole number of rounds
+    ((16, 16, 1 << 20, 2, 8, 2, 16, 8), -2),           # sink too small
+])
+def test_probe_stream_argument_errors(P, args, code):
+    from paged_kv_cache_181_amd import probe
+    p = [ctypes.c_void_p(a) if i in (0, 1, 6) else a for i, a in enumerate(args)]
+    assert probe.lib.pkv_probe_stream_read(*p, None) == code
+    assert probe.lib.pkv_probe_last_error().decode()
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(k=0), -1), (dict(head_dim=64), -3), (dict(hp=3), -3), (dict(waves=12), -3),
+    (dict(hp=8, waves=4), -3), (dict(depth=5), -3), (dict(waves=16, depth=4), -3),
+    (dict(hkv=6, hp=4), -2), (dict(table=2047), -2), (dict(part=24, waves=16), -2),
+    (dict(part=2048), -2), (dict(nb=0), -2), (dict(lds=200 * 1024), -2), (dict(sink=100), -2),
+])
+def test_probe_paged_argument_errors(P, over, code):
+    from paged_kv_cache_181_amd import probe
+    a = dict(k=16, v=16, bt=16, table=2048, nb=2048, hkv=8, head_dim=128, hp=2, waves=8, part=32,
+             depth=2, lds=0, sink=1 << 16)
+    a.update(over)
+    rc = probe.lib.pkv_probe_paged_read(
+        ctypes.c_void_p(a["k"]), ctypes.c_void_p(a["v"]), ctypes.c_void_p(a["bt"]), a["table"],
+        a["nb"], a["hkv"], a["head_dim"], a["hp"], a["waves"], a["part"], a["depth"], a["lds"],
+        ctypes.c_void_p(16), a["sink"], None)
+    assert rc == code, probe.lib.pkv_probe_last_error().decode()
 
 
 @pytest.mark.parametrize("layers,hkv,d", [(32, 8, 128), (1, 2, 64), (80, 8, 128), (32, 32, 128)])
