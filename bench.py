@@ -290,12 +290,13 @@ def cpu_baseline(wl, seconds):
 # and slots from the seeded generator).  Reported beside the headline.
 
 OTHER = {
-    # name: (seed, layers, split partition or 0 for the direct form); the
-    # partition is the caller's choice for these batches: the fastest of a
-    # sweep over direct, 256, 512, 1024 and 2048 on MI355X
-    "tiny": (1, 32, 0),
-    "llama8b_batch": (2, 32, 2048),
-    "spec_verify": (4, 32, 1024),
+    # name: (seed, layers, split partition: None for the direct form, 0 for
+    # the balanced split); the partition is the caller's choice for these
+    # batches: the fastest of a sweep over direct, balanced, 256, 512, 1024
+    # and 2048 on MI355X
+    "tiny": (1, 32, None),
+    "llama8b_batch": (2, 32, 0),
+    "spec_verify": (4, 32, 0),
     "k8v4": (5, 32, 2048),
     "long32k_window2048": (3, 32, 128),
 }
@@ -323,7 +324,8 @@ def other_workload(name, P, W, torch, steps, warmup):
     nv = [rnd(T, Hkv, D) for _ in range(layers)]
     out = [torch.empty(B, Q, Hq, D, dtype=dt, device=dev) for _ in range(layers)]
     ws = None
-    if part:
+    split = part is not None
+    if split:
         span = min(mcl, window + Q + 15) if window else mcl   # a window's grid spans the window
         ws = torch.zeros(P.splitkv_workspace_size(B, Q, Hq, D, span, part) // 4 + 4,
                          dtype=torch.float32, device=dev)
@@ -376,7 +378,7 @@ def other_workload(name, P, W, torch, steps, warmup):
                     P.paged_attention_decode_splitkv_window_append(out[l], q[l], nk[l], nv[l],
                                                                    K[l], V[l], bt, cl, scale, G,
                                                                    window, mcl, part, ws)
-                elif part:
+                elif split:
                     P.paged_attention_decode_splitkv_append(out[l], q[l], nk[l], nv[l], K[l], V[l],
                                                             bt, cl, scale, G, mcl, part, ws)
                 else:
@@ -394,7 +396,8 @@ def other_workload(name, P, W, torch, steps, warmup):
             "pct_of_hbm_peak": round(100 * layer_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
             "decode_rows_per_s": round(B * Q / (ms * 1e-3), 1),
             "layers": layers,
-            "form": (f"split-KV partition {part}" if part else "direct")
+            "form": ("direct" if not split else "balanced split" if part == 0
+                     else f"split-KV partition {part}")
             + (", append form (quantize-on-write in the decode launch)" if name == "k8v4"
                else f", append form, sliding window {window}" if window else ", append form")
             + ", HIP graph",

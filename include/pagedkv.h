@@ -146,8 +146,14 @@ int paged_attention_decode(void* out, int out_dtype, const void* query,
 /*
  * Workspace bytes for the split-KV calls (host-only arithmetic, no GPU use).
  * partition_size is in tokens and must be a positive multiple of block_size
- * (16).  max_context_len bounds context_lens for the grid size; a longer
- * sequence is still handled correctly (its last partition runs to its end).
+ * (16), or 0 for the balanced split (below).  max_context_len bounds
+ * context_lens for the grid size; a longer sequence is still handled
+ * correctly (its last partition runs to its end).
+ *   fixed partitions: batch * q_len * num_q_heads * P * (head_dim + 2) * 4,
+ *                     P = ceil(max_context_len / partition_size);
+ *   balanced split:   (R + batch) * num_q_heads * q_len * (head_dim + 2) * 4,
+ *                     R = 16384 / num_q_heads rounded down to a multiple of 8
+ *                     (max_context_len plays no part).
  */
 int paged_attention_decode_splitkv_workspace_size(int batch, int q_len, int num_q_heads,
                                                   int head_dim, int max_context_len,
@@ -161,6 +167,19 @@ int paged_attention_decode_splitkv_workspace_size(int batch, int q_len, int num_
  * paged_attention_decode (up to fp32 summation order).  The workspace
  * contents on entry do not matter; two calls that overlap in time must not
  * share a workspace.
+ *
+ * partition_size 0 asks for the balanced split (16-bit caches; also accepted
+ * by paged_attention_decode_splitkv_append and
+ * paged_attention_decode_splitkv_noalloc, rejected with PKV_ERR_UNSUPPORTED
+ * by the other split calls).  For each KV head the batch's blocks are laid
+ * end to end in sequence order and cut into R equal runs (R as for the
+ * workspace size), one per wavefront, so every wavefront reads the same
+ * number of blocks however ragged the lengths are (mlxcel "KV Cache", Paged
+ * Decode Storage and Kernels: the decode split count; here the split follows
+ * the batch's total length rather than a fixed partition size).  A run that
+ * crosses sequences leaves one partial per sequence; the merge combines each
+ * row's partials by log-sum-exp as for fixed partitions.  Requires
+ * batch * max_blocks_per_seq < 2^31.
  */
 int paged_attention_decode_splitkv(void* out, int out_dtype, const void* query,
                                    const void* key_cache, const void* value_cache, int kv_dtype,

@@ -99,15 +99,28 @@ int check_attention(void* out, int out_dtype, const void* query, const void* k_c
   return PKV_OK;
 }
 
+// partition_size 0 (where `balanced` allows it) asks for the balanced split:
+// parts = 0 and bytes = its workspace, (runs + batch) * num_q_heads * q_len
+// partial rows of head_dim + 2 floats.
 int split_geometry(int batch, int q_len, int num_q_heads, int head_dim, int max_context_len,
-                   int partition_size, int64_t& parts, size_t& bytes) {
+                   int partition_size, int64_t& parts, size_t& bytes, bool balanced = false) {
   if (batch < 0 || q_len <= 0 || num_q_heads <= 0 || max_context_len < 0)
     return fail(PKV_ERR_SHAPE, "invalid split-KV sizes");
-  if (partition_size <= 0 || partition_size % 16 != 0)
-    return fail(PKV_ERR_UNSUPPORTED, "partition_size must be a positive multiple of 16 (got %d)",
-                partition_size);
   if (head_dim != 64 && head_dim != 128)
     return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  if (partition_size == 0 && balanced) {
+    const int runs = pkv::flat_runs_for(num_q_heads);
+    if (runs < 8 || batch > 65535)
+      return fail(PKV_ERR_UNSUPPORTED, "balanced split: num_q_heads must be at most %d",
+                  pkv::kFlatQueryWaves / 8);
+    parts = 0;
+    bytes = (size_t)((int64_t)(runs + batch) * num_q_heads * q_len * (head_dim + 2) * 4);
+    return PKV_OK;
+  }
+  if (partition_size <= 0 || partition_size % 16 != 0)
+    return fail(PKV_ERR_UNSUPPORTED, "partition_size must be a positive multiple of 16 (got %d)%s",
+                partition_size, partition_size == 0 ? "; 0 (balanced split) is not supported here"
+                                                    : "");
   parts = ((int64_t)max_context_len + partition_size - 1) / partition_size;
   if (parts < 1) parts = 1;
   if (parts > 65535) return fail(PKV_ERR_UNSUPPORTED, "too many partitions (%lld)", (long long)parts);
@@ -117,17 +130,33 @@ int split_geometry(int batch, int q_len, int num_q_heads, int head_dim, int max_
 }
 
 int setup_split(pkv::AttnArgs& a, int head_dim, int max_context_len, int partition_size,
-                void* workspace, size_t workspace_bytes) {
+                void* workspace, size_t workspace_bytes, bool balanced = false) {
   int64_t parts = 0;
   size_t need = 0;
   int rc = split_geometry(a.batch, a.q_len, a.num_q_heads, head_dim, max_context_len,
-                          partition_size, parts, need);
+                          partition_size, parts, need, balanced);
   if (rc) return rc;
   if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace is NULL");
   if (!aligned16(workspace)) return fail(PKV_ERR_ALIGN, "workspace must be 16-byte aligned");
   if (workspace_bytes < need)
     return fail(PKV_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed",
                 workspace_bytes, need);
+  if (parts == 0) {                       // balanced split
+    // flattened block positions are 32-bit in the kernels
+    if ((int64_t)a.batch * a.max_blocks > 0x7fffffffLL)
+      return fail(PKV_ERR_UNSUPPORTED, "balanced split: batch * max_blocks_per_seq above 2^31");
+    const int runs = pkv::flat_runs_for(a.num_q_heads);
+    const int64_t rows = (int64_t)(runs + a.batch) * a.num_q_heads * a.q_len;
+    a.flat_runs = runs;
+    a.num_parts = 1;
+    a.ws_parts = 0;
+    a.part_base = 0;
+    a.part_blocks = a.max_blocks;
+    a.ws_o = (float*)workspace;
+    a.ws_m = a.ws_o + rows * head_dim;
+    a.ws_l = a.ws_m + rows;
+    return PKV_OK;
+  }
   const int64_t rows = (int64_t)a.batch * a.q_len * a.num_q_heads;
   a.num_parts = (int)parts;
   a.ws_parts = (int)parts;
@@ -296,7 +325,7 @@ int paged_attention_decode_splitkv_workspace_size(int batch, int q_len, int num_
   int64_t parts = 0;
   size_t bytes = 0;
   int rc = split_geometry(batch, q_len, num_q_heads, head_dim, max_context_len, partition_size,
-                          parts, bytes);
+                          parts, bytes, true);
   if (rc) return rc;
   *out_bytes = bytes;
   return ok();
@@ -318,7 +347,7 @@ int paged_attention_decode_splitkv(void* out, int out_dtype, const void* query,
                            head_dim, block_size, num_blocks, scale, a);
   if (rc) return rc;
   if (batch == 0) return ok();
-  rc = setup_split(a, head_dim, max_context_len, partition_size, workspace, workspace_bytes);
+  rc = setup_split(a, head_dim, max_context_len, partition_size, workspace, workspace_bytes, true);
   if (rc) return rc;
   return launch_result(pkv::launch_attention(a, kv_dtype, kv_dtype, head_dim, (hipStream_t)stream),
                        "paged_attention_decode_splitkv");
@@ -343,7 +372,7 @@ int paged_attention_decode_splitkv_noalloc(void* out, int out_dtype, const void*
   int64_t parts = 0;
   size_t need = 0;
   rc = split_geometry(batch, q_len, num_q_heads, head_dim, max_context_len, partition_size, parts,
-                      need);
+                      need, true);
   if (rc) return rc;
   if (need > (size_t)PKV_NOALLOC_SCRATCH_BYTES)
     return fail(PKV_ERR_WORKSPACE,
@@ -353,7 +382,7 @@ int paged_attention_decode_splitkv_noalloc(void* out, int out_dtype, const void*
   void* ws = nullptr;
   rc = scratch_address(&ws);
   if (rc) return rc;
-  rc = setup_split(a, head_dim, max_context_len, partition_size, ws, PKV_NOALLOC_SCRATCH_BYTES);
+  rc = setup_split(a, head_dim, max_context_len, partition_size, ws, PKV_NOALLOC_SCRATCH_BYTES, true);
   if (rc) return rc;
   return launch_result(pkv::launch_attention(a, kv_dtype, kv_dtype, head_dim, (hipStream_t)stream),
                        "paged_attention_decode_splitkv_noalloc");
@@ -629,7 +658,7 @@ int paged_attention_decode_splitkv_append(void* out, int out_dtype, const void* 
   if (!new_key || !new_value) return fail(PKV_ERR_NULL, "new_key / new_value is NULL");
   if (!aligned16(new_key) || !aligned16(new_value))
     return fail(PKV_ERR_ALIGN, "new_key and new_value must be 16-byte aligned");
-  rc = setup_split(a, head_dim, max_context_len, partition_size, workspace, workspace_bytes);
+  rc = setup_split(a, head_dim, max_context_len, partition_size, workspace, workspace_bytes, true);
   if (rc) return rc;
   a.new_k = new_key;
   a.new_v = new_value;

@@ -1003,6 +1003,402 @@ void attn_partition_kernel(const AttnArgs a) {
 }
 
 // ------------------------------------------------------------------------------
+// Balanced split-KV (partition_size 0; 16-bit caches, plain and append forms).
+//
+// For each KV head the batch's blocks are laid end to end: sequence b's blocks
+// 0 .. nblk_b - 1 (nblk_b = ceil(L_b / 16), L_b clamped like every length)
+// follow those of sequences 0 .. b-1, T blocks in all.  The T blocks are cut
+// into S equal runs, one per wavefront (run s covers flattened blocks
+// [s * per, (s+1) * per), per = ceil(T / S)), so every wavefront streams the
+// same number of blocks however ragged the lengths; with fixed-size
+// partitions the longest ones set the launch's end while most CUs sit idle.
+// A run may cross sequence boundaries: the wave attends each sequence's piece
+// of it (a segment) and writes one partial per segment, to slot s + b of its
+// KV head.  No two segments share a slot: walking the flattened blocks, each
+// new segment starts a new run, a new sequence, or both, so s + b grows with
+// every segment.  The merge kernel finds a row's slots from the same lengths.
+// There is no merge inside the workgroup; waves h*NWH .. of a workgroup take
+// KV head HP*blockIdx.y + h and runs blockIdx.x*NWH + (w % NWH), so with HP = 2
+// the two heads' waves read the same blocks together.
+//
+// Workspace: o[Hkv][S + B][G*Q][D] (unnormalised), m[..][G*Q], l[..][G*Q],
+// tile row r of a slot being query row (i = r / G, head g*G + r % G).
+
+// Built for three waves per SIMD in the 4-row form (up to 168 registers) and
+// two in the 16-row form, which holds more per lane.
+template <Fmt KV, int D, int RT, int HP>
+__global__ __launch_bounds__((Shape<KV, RT>::NW * kWave), (RT == 4 ? 3 : 2))
+void attn_flat_kernel(const AttnArgs a) {
+  using MM = Mma<KV>;
+  static_assert(KV != Fmt::K8V4, "balanced split: 16-bit caches");
+  constexpr int NW = Shape<KV, RT>::NW;
+  constexpr int NWH = NW / HP;
+  constexpr int KS = D / 32, NT = D / 16;
+  constexpr int QSTR = D + 8;
+  __shared__ __align__(16) unsigned char v_s[NW * 16 * D * 2];
+  __shared__ __align__(16) uint16_t q_s[NW * RT * QSTR];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hw = w / NWH;
+  const int g = blockIdx.y * HP + hw;                       // KV head
+  const int S = a.flat_runs;
+  const int s = blockIdx.x * NWH + w % NWH;                 // this wave's run
+  const int rho = lane & 15, qd = lane >> 4;
+  const int Q = a.q_len, G = a.gqa, GQ = G * Q, Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+  const int B = a.batch;
+  const int cap = a.max_blocks * kBlock;
+  const bool append = a.new_k != nullptr;
+
+  // ---- lengths, 64 sequences per chunk (lane i: sequence base + i), and
+  // the flattened end of each: ends are inclusive prefix sums of nblk
+  auto chunk_lens = [&](int base, int& len, int& end, int carry) {
+    const int b = base + lane;
+    int L = b < B ? a.context_lens[b] : 0;
+    L = min(max(L, 0), cap);
+    len = L;
+    int v = (L + kBlock - 1) / kBlock;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int t = __shfl_up(v, d, kWave);
+      if (lane >= d) v += t;
+    }
+    end = carry + v;
+  };
+  int base = 0, len_c = 0, end_c = 0;
+  chunk_lens(0, len_c, end_c, 0);
+  // (readlane, not a shuffle, so the compiler knows these values are
+  // wave-uniform and keeps the segment loop in scalar control flow)
+  int T = __builtin_amdgcn_readlane(end_c, kWave - 1);
+  for (int bb = kWave; bb < B; bb += kWave) {               // batches past 64 sequences
+    int l2, e2;
+    chunk_lens(bb, l2, e2, T);
+    T = __builtin_amdgcn_readlane(e2, kWave - 1);
+  }
+  const int per = (T + S - 1) / S;
+  const int r0 = min(s * per, T), r1 = min(r0 + per, T);
+  if (r0 >= r1) return;                                      // nothing left for this run
+  // the chunk holding the first sequence that ends past r0 (one exists, since
+  // r0 < T; the bound on base only makes the loop's end evident)
+  uint64_t past = __builtin_amdgcn_ballot_w64(base + lane < B && end_c > r0);
+  while (past == 0) {
+    const int carry = __builtin_amdgcn_readlane(end_c, kWave - 1);
+    base += kWave;
+    if (base >= B) return;
+    chunk_lens(base, len_c, end_c, carry);
+    past = __builtin_amdgcn_ballot_w64(base + lane < B && end_c > r0);
+  }
+  int b = base + __builtin_ctzll(past);
+
+  const LaneOffsets<KV, D> loff(Hkv, g, rho, qd);
+  unsigned char* vst = v_s + w * (16 * D * 2);
+  uint16_t* qw = q_s + w * RT * QSTR;
+  const uint16_t* qrow = qw + (rho < GQ ? rho : rho % GQ) * QSTR;
+  const int tr_off = ((((rho & 3) >> 1) * 16) + 4 * qd + (rho >> 2)) * 16 + (rho & 1) * 8;
+  const float sl2 = a.scale_log2;
+  const int64_t slot_base = (int64_t)g * (S + B);
+  constexpr int QCW = RT * (D / 8);                          // 16-byte query chunks per wave
+  constexpr int QPL = (QCW + kWave - 1) / kWave;
+
+  // the lengths chunk holding sequence b (b only grows)
+  auto chunk_of = [&]() {
+    while (b - base >= kWave) {
+      const int carry = __builtin_amdgcn_readlane(end_c, kWave - 1);
+      base += kWave;
+      chunk_lens(base, len_c, end_c, carry);
+    }
+  };
+  for (int pos = r0; pos < r1;) {
+    // sequence b covers flattened blocks [end_b - nblk_b, end_b); skip empty ones
+    chunk_of();
+    int end_b = __builtin_amdgcn_readlane(end_c, b - base);
+    while (end_b <= pos) {
+      if (++b >= B) return;                                  // (not reached: pos < T)
+      chunk_of();
+      end_b = __builtin_amdgcn_readlane(end_c, b - base);
+    }
+    const int L = __builtin_amdgcn_readlane(len_c, b - base);
+    const int start_b = end_b - (L + kBlock - 1) / kBlock;
+    const int seg_end = min(r1, end_b);
+    const int jb0 = pos - start_b, n = seg_end - pos;        // the segment's blocks of b
+
+    // the segment's table entries (64 per chunk), query rows and new rows
+    const auto btr = span_rsrc(a.block_tables + (int64_t)b * a.max_blocks,
+                               (uint32_t)a.max_blocks * 4u);
+    int tbl = lane < n ? buf_load<int>(btr, (uint32_t)(jb0 + lane) * 4u) : 0;
+    u4 qv[QPL];
+#pragma unroll
+    for (int u = 0; u < QPL; ++u) {
+      const int idx = lane + u * kWave;
+      const int r = idx / (D / 8), c8 = idx % (D / 8);
+      qv[u] = u4{0u, 0u, 0u, 0u};
+      if (idx < QCW && r < GQ)
+        qv[u] = *(const u4*)((const uint16_t*)a.q +
+                             (((int64_t)b * Q + r / G) * Hq + g * G + r % G) * D + 8 * c8);
+    }
+    const uint32_t new_bytes = append ? (uint32_t)(Q * Hkv * D * 2) : 0u;
+    const auto nkr = span_rsrc((const char*)a.new_k + (append ? (int64_t)b * Q * Hkv * D * 2 : 0),
+                               new_bytes);
+    const auto nvr = span_rsrc((const char*)a.new_v + (append ? (int64_t)b * Q * Hkv * D * 2 : 0),
+                               new_bytes);
+    const int first_new = append ? L - Q : L;                // positions from here on are new rows
+
+    // block j of the current table chunk (first segment block jbase): loads
+    // its rows (new tokens' rows from the new K/V input) and returns the mask
+    // of its tokens that hold data
+    auto fetch = [&](int j, int cnt, int jbase, BlockRegs<KV, D>& br) -> uint32_t {
+      const int pb = __builtin_amdgcn_readlane(tbl, j & 63);
+      const bool ok = j < cnt && pb >= 0 && (int64_t)pb < a.num_blocks;
+      load_block<KV, D>(a, ok ? pb : 0, ok, loff, br);
+      const int jb = (jbase + j) * kBlock;
+      if (ok && jb + kBlock > first_new) {                    // wave-uniform: new tokens here
+        const int t = jb + rho - first_new;
+        if (t >= 0 && t < Q) {
+          const uint32_t off = (uint32_t)(((t * Hkv + g) * D + 8 * qd) * 2);
+#pragma unroll
+          for (int m = 0; m < KS; ++m) br.k[m] = buf_load<u4>(nkr, off + 64 * m);
+#pragma unroll
+          for (int m = 0; m < KS; ++m) br.v[m] = buf_load<u4>(nvr, off + 64 * m);
+        }
+      }
+      const int left = L - jb;
+      const uint32_t msk = left >= kBlock ? 0xffffu : (1u << max(left, 0)) - 1u;
+      return ok ? msk : 0u;
+    };
+
+    // stage the query rows (this wave's copy) behind the first loads
+    BlockRegs<KV, D> r0s, r1s;
+    const int cnt0 = min(64, n);
+    uint32_t ok0 = fetch(0, cnt0, jb0, r0s), ok1 = 0u;
+#pragma unroll
+    for (int u = 0; u < QPL; ++u) {
+      const int idx = lane + u * kWave;
+      if (idx < QCW) *(u4*)(qw + (idx / (D / 8)) * QSTR + 8 * (idx % (D / 8))) = qv[u];
+    }
+    wave_lds_fence();
+
+    const bool row_ok = rho < GQ;
+    const int iq = row_ok ? rho / G : 0;
+    const int nvis = row_ok ? (L - Q + iq + 1) : L;          // visible positions of the row
+    const int full_lim = L - Q + 1;                          // every row sees j < full_lim
+    float m_run = kNegInf, l_run = 0.f;
+    f4 o[NT];
+#pragma unroll
+    for (int nn = 0; nn < NT; ++nn) o[nn] = f4{0.f, 0.f, 0.f, 0.f};
+
+    // one tile: the new rows go to their cache slots, V into LDS, S^T = K Q^T,
+    // then the online softmax and O^T += V^T P^T, as in the partition kernel
+    auto process = [&](int j, int jbase, uint32_t vmask, BlockRegs<KV, D>& br) {
+      const int j0 = (jbase + j) * kBlock;
+      if (append && vmask != 0u && j0 + kBlock > first_new) { // wave-uniform
+        const int t = j0 + rho - first_new;
+        if (t >= 0 && t < Q) {
+          const int pb = __builtin_amdgcn_readlane(tbl, j & 63);
+          const int64_t row = ((int64_t)pb * kBlock + rho) * Hkv + g;
+          char* kd = (char*)a.k_cache + row * (D * 2) + 16 * qd;
+          char* vd = (char*)a.v_cache + row * (D * 2) + 16 * qd;
+#pragma unroll
+          for (int m = 0; m < KS; ++m) {
+            *(u4*)(kd + 64 * m) = br.k[m];
+            *(u4*)(vd + 64 * m) = br.v[m];
+          }
+        }
+      }
+      const bool tail = vmask != 0xffffu;
+      const bool tok_ok = (vmask >> rho) & 1u;
+#pragma unroll
+      for (int m = 0; m < KS; ++m) {
+        u4 vv = br.v[m];
+        if (tail && !tok_ok) vv = u4{0u, 0u, 0u, 0u};         // 0 * NaN is NaN
+        *(u4*)(vst + m * 1024 + lane * 16) = vv;
+      }
+      f4 sc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < KS; ++m) sc = MM::qk(br.k[m], *(const u4*)(qrow + 32 * m + 8 * qd), sc);
+      wave_lds_fence();
+      float sv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[r] = sc[r] * sl2;
+      if (tail || j0 + kBlock > full_lim) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int jj = j0 + 4 * qd + r;
+          if (!((vmask >> (4 * qd + r)) & 1u) || jj >= nvis) sv[r] = kNegInf;
+        }
+      }
+      const float mx = quarter_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+      const bool grow = mx > m_run + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mx : m_run;
+        const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
+#pragma unroll
+        for (int nn = 0; nn < NT; ++nn) o[nn] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = m_run == kNegInf ? 0.f : m_run;
+      float pr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sv[r] - m_use);
+      l_run += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      u2 phi, plo;
+      MM::split(pr, phi, plo);
+#pragma unroll
+      for (int nn = 0; nn < NT; ++nn) {
+        const u2 av = lds_read_tr16(vst + tr_off + (nn >> 1) * 1024 + (nn & 1) * 512);
+        o[nn] = MM::pv(av, phi, o[nn]);
+        o[nn] = MM::pv(av, plo, o[nn]);
+      }
+      wave_lds_fence();
+    };
+
+    // ---- the segment's blocks, 64 table entries at a time; two register
+    // sets, the next block's loads issued before the current block is used
+    for (int c0 = 0; c0 < n; c0 += 64) {
+      const int cnt = min(64, n - c0);
+      if (c0 > 0) {
+        tbl = lane < cnt ? buf_load<int>(btr, (uint32_t)(jb0 + c0 + lane) * 4u) : 0;
+        ok0 = fetch(0, cnt, jb0 + c0, r0s);
+      }
+      for (int k = 0; k < cnt; k += 2) {
+        ok1 = fetch(k + 1, cnt, jb0 + c0, r1s);
+        process(k, jb0 + c0, ok0, r0s);
+        ok0 = fetch(k + 2, cnt, jb0 + c0, r0s);
+        if (k + 1 < cnt) process(k + 1, jb0 + c0, ok1, r1s);
+      }
+    }
+
+    // ---- this segment's partial, straight from the registers: lane (rho, qd)
+    // holds row rho's dims 16 n + 4 qd .. +3
+    l_run = quarter_sum(l_run);
+    if (row_ok) {
+      const int64_t pi = (slot_base + s + b) * GQ + rho;
+      float* od = a.ws_o + pi * D + 4 * qd;
+#pragma unroll
+      for (int nn = 0; nn < NT; ++nn) *(f4*)(od + 16 * nn) = o[nn];
+      if (qd == 0) {
+        a.ws_m[pi] = m_run;
+        a.ws_l[pi] = l_run;
+      }
+    }
+    wave_lds_fence();                  // the next segment rewrites this wave's query rows
+    pos = seg_end;
+    ++b;
+  }
+}
+
+// Merge of the balanced split's partials: one workgroup per output row
+// (b, i, h).  The row's slots are s + b for the runs s that hold a block of
+// sequence b, found from the same lengths as the partition pass; then the
+// same single-pass log-sum-exp fold as attn_merge_kernel.
+template <int D>
+__global__ __launch_bounds__(256) void attn_flat_merge_kernel(const AttnArgs a) {
+  constexpr int NC = D / 4;
+  constexpr int NG = 256 / NC;
+  __shared__ f4 acc_s[NG][NC];
+  __shared__ float m_s[NG], den_s[NG];
+  __shared__ int geo_s[2];               // the row's first slot and slot count
+
+  const int64_t row = blockIdx.x;
+  const int t = threadIdx.x;
+  const int Q = a.q_len, Hq = a.num_q_heads, G = a.gqa, GQ = G * Q, B = a.batch;
+  const int h = (int)(row % Hq), i = (int)((row / Hq) % Q), b = (int)(row / ((int64_t)Hq * Q));
+  const int g = h / G, rr = i * G + h % G;
+  const int S = a.flat_runs;
+  const int cap = a.max_blocks * kBlock;
+  if (t < kWave) {                       // wave 0: T and the blocks before sequence b
+    int tot = 0, before = 0;
+    for (int base = 0; base < B; base += kWave) {
+      const int bi = base + t;
+      int L = bi < B ? a.context_lens[bi] : 0;
+      L = min(max(L, 0), cap);
+      const int nb = (L + kBlock - 1) / kBlock;
+      int v = nb, vb = bi < b ? nb : 0;
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        v += __shfl_xor(v, d, kWave);
+        vb += __shfl_xor(vb, d, kWave);
+      }
+      tot += v;
+      before += vb;
+    }
+    if (t == 0) {
+      const int L = min(max(a.context_lens[b], 0), cap);
+      const int nb_b = (L + kBlock - 1) / kBlock;
+      const int per = (tot + S - 1) / S;
+      int first = 0, count = 0;
+      if (per > 0 && nb_b > 0) {                           // runs holding a block of b
+        first = before / per;
+        count = (before + nb_b - 1) / per - first + 1;
+      }
+      geo_s[0] = first + b;
+      geo_s[1] = count;
+    }
+  }
+  __syncthreads();
+  const int np = geo_s[1];
+  const int64_t pbase = ((int64_t)g * (S + B) + geo_s[0]) * GQ + rr;   // the row's first partial
+  const float* wm = a.ws_m + pbase;
+  const float* wl = a.ws_l + pbase;
+  const float* wo = a.ws_o + pbase * D;
+  const int64_t ps = GQ;                                    // partial stride (rows)
+
+  const int c = t % NC, grp = t / NC;
+  float m_t = kNegInf, den = 0.f;
+  f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+  constexpr int U = 4;
+  for (int p0 = grp; p0 < np; p0 += U * NG) {
+    float mp[U], lp[U];
+    f4 op[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int pp = min(p0 + u * NG, np - 1);
+      mp[u] = wm[pp * ps];
+      lp[u] = wl[pp * ps];
+      op[u] = *(const f4*)(wo + pp * ps * D + 4 * c);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) asm volatile("" : "+v"(mp[u]), "+v"(lp[u]), "+v"(op[u]));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool use = p0 + u * NG < np && mp[u] != kNegInf;
+      const float m_new = use ? fmaxf(m_t, mp[u]) : m_t;
+      const float e_old = m_t == kNegInf ? 0.f : fast_exp2(m_t - m_new);
+      const float e_new = use ? fast_exp2(mp[u] - m_new) : 0.f;
+      const f4 o_u = use ? op[u] : f4{0.f, 0.f, 0.f, 0.f};
+      const float l_u = use ? lp[u] : 0.f;
+      acc = acc * e_old + o_u * e_new;
+      den = den * e_old + l_u * e_new;
+      m_t = m_new;
+    }
+  }
+  acc_s[grp][c] = acc;
+  if (c == 0) {
+    m_s[grp] = m_t;
+    den_s[grp] = den;
+  }
+  __syncthreads();
+  if (t < NC) {
+    float M = kNegInf;
+#pragma unroll
+    for (int gg = 0; gg < NG; ++gg) M = fmaxf(M, m_s[gg]);
+    f4 tot = f4{0.f, 0.f, 0.f, 0.f};
+    float dt = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int gg = 0; gg < NG; ++gg) {
+        const float e = m_s[gg] == kNegInf ? 0.f : fast_exp2(m_s[gg] - M);
+        tot += acc_s[gg][t] * e;
+        dt += den_s[gg] * e;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      store_out(a.out, (OutT)a.out_dtype, row * D + 4 * t + r, dt > 0.f ? tot[r] / dt : 0.f);
+  }
+}
+
+// ------------------------------------------------------------------------------
 // Sparse-V partition kernel (approximate; 16-bit caches, G*q_len <= 4).
 //
 // The V row of position j is read only when some query row of the KV head has
@@ -1387,8 +1783,43 @@ static int device_cu_count() {
   return cached[dev] > 0 ? cached[dev] : 0;
 }
 
+// Balanced split: grid (runs / waves per head, KV heads / HP), then the merge.
+template <Fmt KV, int D>
+static hipError_t launch_flat(const AttnArgs& a, hipStream_t stream) {
+  if constexpr (KV == Fmt::K8V4) {
+    return hipErrorInvalidValue;
+  } else {
+    const int rows = a.gqa * a.q_len;
+    const int hp = a.num_kv_heads % 2 == 0 ? 2 : 1;
+    if (rows <= 4) {
+      constexpr int NW = Shape<KV, 4>::NW;
+      const dim3 grid((unsigned)(a.flat_runs / (NW / hp)), (unsigned)(a.num_kv_heads / hp));
+      if (hp == 2)
+        hipLaunchKernelGGL((attn_flat_kernel<KV, D, 4, 2>), grid, dim3(NW * kWave), 0, stream, a);
+      else
+        hipLaunchKernelGGL((attn_flat_kernel<KV, D, 4, 1>), grid, dim3(NW * kWave), 0, stream, a);
+    } else {
+      constexpr int NW = Shape<KV, 16>::NW;
+      const dim3 grid((unsigned)(a.flat_runs / (NW / hp)), (unsigned)(a.num_kv_heads / hp));
+      if (hp == 2)
+        hipLaunchKernelGGL((attn_flat_kernel<KV, D, 16, 2>), grid, dim3(NW * kWave), 0, stream, a);
+      else
+        hipLaunchKernelGGL((attn_flat_kernel<KV, D, 16, 1>), grid, dim3(NW * kWave), 0, stream, a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned out_rows = (unsigned)((int64_t)a.batch * a.q_len * a.num_q_heads);
+    hipLaunchKernelGGL((attn_flat_merge_kernel<D>), dim3(out_rows), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+}
+
 template <Fmt KV, Fmt QT, int D>
 static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream, int stage) {
+  if (a.flat_runs > 0) {
+    if (stage != STAGE_ALL || a.mode != 0 || a.window != 0) return hipErrorInvalidValue;
+    return launch_flat<KV, D>(a, stream);
+  }
   if (stage != STAGE_MERGE) {
     const int rows = (a.mode == 1 ? a.group_size : 1) * a.gqa * a.q_len;
     dim3 grid((unsigned)a.num_parts, (unsigned)a.num_kv_heads,

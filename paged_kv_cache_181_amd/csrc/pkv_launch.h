@@ -55,7 +55,16 @@ struct AttnArgs {
   int num_groups, group_size;
   float v_log2_threshold;        // sparse-V: skip V rows below 2^this of the running max
   unsigned long long* v_rows_read;   // sparse-V: optional device counter of V rows read
+  int flat_runs;                 // balanced split: runs (wavefronts) per KV head; 0 = off
 };
+
+// Balanced split (partition_size 0): each KV head's flattened blocks are cut
+// into flat_runs_for(Hq) equal runs, one per wavefront.  The workspace holds
+// (runs + batch) * num_q_heads * q_len partial rows of head_dim + 2 floats.
+constexpr int kFlatQueryWaves = 16384;
+constexpr int flat_runs_for(int num_q_heads) {
+  return num_q_heads > 0 ? (kFlatQueryWaves / num_q_heads) / 8 * 8 : 0;
+}
 
 // kv_fmt: 0 f16, 1 bf16, 3 k8v4; q_fmt: 0 f16, 1 bf16 (must equal kv_fmt unless k8v4).
 // stage: STAGE_ALL launches the partition kernel and, for the split form, the

@@ -176,7 +176,23 @@ def test_splitkv_workspace_errors(P):
     assert lib.paged_attention_decode_splitkv(*base, 64, 512, FAKE, 10, None) == -4
     assert "too small" in P.last_error()
     assert lib.paged_attention_decode_splitkv(*base, 64, 24, FAKE, 1 << 30, None) == -3
-    assert lib.paged_attention_decode_splitkv(*base, 64, 0, FAKE, 1 << 30, None) == -3
+    assert lib.paged_attention_decode_splitkv(*base, 64, -16, FAKE, 1 << 30, None) == -3
+    # partition_size 0 is the balanced split, with its own workspace size:
+    # (runs + batch) * num_q_heads * q_len partial rows of head_dim + 2 floats,
+    # runs = 16384 / num_q_heads rounded down to a multiple of 8
+    size = ctypes.c_size_t(0)
+    assert lib.paged_attention_decode_splitkv_workspace_size(2, 1, 32, 128, 64, 0,
+                                                             ctypes.byref(size)) == 0
+    assert size.value == (512 + 2) * 32 * 130 * 4
+    assert lib.paged_attention_decode_splitkv_workspace_size(3, 4, 6, 64, 9, 0,
+                                                             ctypes.byref(size)) == 0
+    assert size.value == (2728 + 3) * 6 * 4 * 66 * 4
+    assert lib.paged_attention_decode_splitkv(*base, 64, 0, FAKE, (512 + 2) * 32 * 130 * 4 - 16,
+                                              None) == -4
+    # the calls without a balanced form reject it before any launch
+    assert lib.paged_attention_decode_splitkv_window(*base, 0, 64, 0, FAKE, 1 << 30, None) == -3
+    assert lib.paged_attention_decode_splitkv_partials(*base[2:], 64, 0, FAKE, 1 << 30, None) == -3
+    assert "balanced" in P.last_error()
 
 
 def test_write_argument_errors(P):

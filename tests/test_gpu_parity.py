@@ -483,26 +483,29 @@ def test_append_long32k_bench_launch_configuration(P):
     assert np.array_equal(dev_to_bits(k), kc) and np.array_equal(dev_to_bits(v), vc)
 
 
-def test_llama8b_append_bench_launch_configuration(P):
+@pytest.mark.parametrize("psize", [0, 2048])
+def test_llama8b_append_bench_launch_configuration(P, psize):
     """The Llama-3-8B-shaped batch as the bench times it: all 32 sequences,
-    append form, split-KV partition 2048 (512 one-head workgroups, so the
-    head-pair form runs), bf16 output."""
+    append form, the balanced split (partition_size 0), bf16 output; and at
+    the fixed 2048-token partitions (512 one-head workgroups, so the head-pair
+    form runs) it was timed at before."""
     case, (ref, kc, vc) = get_append_case("llama8b_batch")
     dc = DevCase(case)
-    out, k, v = run_append(P, dc, split=True, psize=2048, out_dtype=torch.bfloat16)
+    out, k, v = run_append(P, dc, split=True, psize=psize, out_dtype=torch.bfloat16)
     assert np.array_equal(dev_to_bits(k), kc) and np.array_equal(dev_to_bits(v), vc)
     assert max_err(out, ref) <= TOL
 
 
-def test_spec_verify_append_bench_launch_configuration(P):
+@pytest.mark.parametrize("psize", [0, 1024])
+def test_spec_verify_append_bench_launch_configuration(P, psize):
     """The verify batch as the bench times it: all 64 sequences, append form,
-    split-KV partition 1024, bf16 output."""
+    the balanced split, bf16 output (and the fixed 1024-token partitions)."""
     case, _ = get_case("spec_verify")
     ref, kc, vc = oracle.decode_append(case.query, case.new_key, case.new_value, case.key_cache,
                                        case.value_cache, case.block_tables, case.context_lens,
                                        case.scale, case.gqa_factor, case.fmt)
     dc = DevCase(case)
-    out, k, v = run_append(P, dc, split=True, psize=1024, out_dtype=torch.bfloat16)
+    out, k, v = run_append(P, dc, split=True, psize=psize, out_dtype=torch.bfloat16)
     assert np.array_equal(dev_to_bits(k), kc) and np.array_equal(dev_to_bits(v), vc)
     assert max_err(out, ref) <= TOL
 
