@@ -145,6 +145,9 @@ int setup_split(pkv::AttnArgs& a, int head_dim, int max_context_len, int partiti
     // flattened block positions are 32-bit in the kernels
     if ((int64_t)a.batch * a.max_blocks > 0x7fffffffLL)
       return fail(PKV_ERR_UNSUPPORTED, "balanced split: batch * max_blocks_per_seq above 2^31");
+    // the merge runs one 512-thread workgroup per (sequence, KV head)
+    if ((int64_t)a.batch * a.num_kv_heads * 512 > 0xffffffffLL)
+      return fail(PKV_ERR_UNSUPPORTED, "balanced split: batch * num_kv_heads above 2^23");
     const int runs = pkv::flat_runs_for(a.num_q_heads);
     const int64_t rows = (int64_t)(runs + a.batch) * a.num_q_heads * a.q_len;
     a.flat_runs = runs;

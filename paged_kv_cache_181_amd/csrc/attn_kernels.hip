@@ -1287,23 +1287,27 @@ void attn_flat_kernel(const AttnArgs a) {
   }
 }
 
-// Merge of the balanced split's partials: one workgroup per output row
-// (b, i, h).  The row's slots are s + b for the runs s that hold a block of
-// sequence b, found from the same lengths as the partition pass; then the
-// same single-pass log-sum-exp fold as attn_merge_kernel.
-template <int D>
-__global__ __launch_bounds__(256) void attn_flat_merge_kernel(const AttnArgs a) {
-  constexpr int NC = D / 4;
-  constexpr int NG = 256 / NC;
-  __shared__ f4 acc_s[NG][NC];
-  __shared__ float m_s[NG], den_s[NG];
-  __shared__ int geo_s[2];               // the row's first slot and slot count
+// Merge of the balanced split's partials: one workgroup per (sequence b, KV
+// head g), covering the G*q_len rows of that pair, which share their slots:
+// s + b for the runs s that hold a block of sequence b, found from the same
+// lengths as the partition pass.  Thread (item, grp), item = (row, 4-dim
+// chunk), folds slots grp, grp + NG, ... into a running (max, sum, acc) with
+// their loads in flight together; the NG running states of an item are then
+// combined in LDS, as in attn_merge_kernel.
+constexpr int kFlatMergeThreads = 512;
 
-  const int64_t row = blockIdx.x;
+template <int D>
+__global__ __launch_bounds__(kFlatMergeThreads) void attn_flat_merge_kernel(const AttnArgs a) {
+  constexpr int NC = D / 4;                                 // float4 chunks per row
+  constexpr int NT = kFlatMergeThreads;
+  __shared__ f4 acc_s[NT];
+  __shared__ float m_s[NT], den_s[NT];
+  __shared__ int geo_s[2];                                  // the first slot and the slot count
+
   const int t = threadIdx.x;
   const int Q = a.q_len, Hq = a.num_q_heads, G = a.gqa, GQ = G * Q, B = a.batch;
-  const int h = (int)(row % Hq), i = (int)((row / Hq) % Q), b = (int)(row / ((int64_t)Hq * Q));
-  const int g = h / G, rr = i * G + h % G;
+  const int Hkv = a.num_kv_heads;
+  const int b = (int)(blockIdx.x / Hkv), g = (int)(blockIdx.x % Hkv);
   const int S = a.flat_runs;
   const int cap = a.max_blocks * kBlock;
   if (t < kWave) {                       // wave 0: T and the blocks before sequence b
@@ -1337,64 +1341,62 @@ __global__ __launch_bounds__(256) void attn_flat_merge_kernel(const AttnArgs a) 
   }
   __syncthreads();
   const int np = geo_s[1];
-  const int64_t pbase = ((int64_t)g * (S + B) + geo_s[0]) * GQ + rr;   // the row's first partial
-  const float* wm = a.ws_m + pbase;
-  const float* wl = a.ws_l + pbase;
-  const float* wo = a.ws_o + pbase * D;
-  const int64_t ps = GQ;                                    // partial stride (rows)
-
-  const int c = t % NC, grp = t / NC;
+  const int NI = GQ * NC;                                   // items (at most 16 * 32 = NT)
+  const int NG = NT / NI;                                   // thread groups per item
+  const int item = t % NI, grp = t / NI;
+  const int rr = item / NC, c = item % NC;                  // tile row, chunk
+  const int64_t p0 = ((int64_t)g * (S + B) + geo_s[0]) * GQ + rr;   // the row's first partial
   float m_t = kNegInf, den = 0.f;
   f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 4;
-  for (int p0 = grp; p0 < np; p0 += U * NG) {
-    float mp[U], lp[U];
-    f4 op[U];
+  if (grp < NG) {
+    constexpr int U = 8;
+    for (int q0 = grp; q0 < np; q0 += U * NG) {
+      float mp[U], lp[U];
+      f4 op[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int pp = min(p0 + u * NG, np - 1);
-      mp[u] = wm[pp * ps];
-      lp[u] = wl[pp * ps];
-      op[u] = *(const f4*)(wo + pp * ps * D + 4 * c);
-    }
+      for (int u = 0; u < U; ++u) {      // loads first (clamped index), no branches between
+        const int64_t pi = p0 + (int64_t)min(q0 + u * NG, np - 1) * GQ;
+        mp[u] = a.ws_m[pi];
+        lp[u] = a.ws_l[pi];
+        op[u] = *(const f4*)(a.ws_o + pi * D + 4 * c);
+      }
 #pragma unroll
-    for (int u = 0; u < U; ++u) asm volatile("" : "+v"(mp[u]), "+v"(lp[u]), "+v"(op[u]));
+      for (int u = 0; u < U; ++u) asm volatile("" : "+v"(mp[u]), "+v"(lp[u]), "+v"(op[u]));
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool use = p0 + u * NG < np && mp[u] != kNegInf;
-      const float m_new = use ? fmaxf(m_t, mp[u]) : m_t;
-      const float e_old = m_t == kNegInf ? 0.f : fast_exp2(m_t - m_new);
-      const float e_new = use ? fast_exp2(mp[u] - m_new) : 0.f;
-      const f4 o_u = use ? op[u] : f4{0.f, 0.f, 0.f, 0.f};
-      const float l_u = use ? lp[u] : 0.f;
-      acc = acc * e_old + o_u * e_new;
-      den = den * e_old + l_u * e_new;
-      m_t = m_new;
+      for (int u = 0; u < U; ++u) {
+        const bool use = q0 + u * NG < np && mp[u] != kNegInf;
+        const float m_new = use ? fmaxf(m_t, mp[u]) : m_t;
+        const float e_old = m_t == kNegInf ? 0.f : fast_exp2(m_t - m_new);
+        const float e_new = use ? fast_exp2(mp[u] - m_new) : 0.f;
+        const f4 o_u = use ? op[u] : f4{0.f, 0.f, 0.f, 0.f};
+        const float l_u = use ? lp[u] : 0.f;
+        acc = acc * e_old + o_u * e_new;
+        den = den * e_old + l_u * e_new;
+        m_t = m_new;
+      }
     }
   }
-  acc_s[grp][c] = acc;
-  if (c == 0) {
-    m_s[grp] = m_t;
-    den_s[grp] = den;
-  }
+  acc_s[t] = acc;
+  m_s[t] = m_t;
+  den_s[t] = den;
   __syncthreads();
-  if (t < NC) {
+  if (t < NI) {
     float M = kNegInf;
-#pragma unroll
-    for (int gg = 0; gg < NG; ++gg) M = fmaxf(M, m_s[gg]);
+    for (int gg = 0; gg < NG; ++gg) M = fmaxf(M, m_s[gg * NI + t]);
     f4 tot = f4{0.f, 0.f, 0.f, 0.f};
     float dt = 0.f;
     if (M != kNegInf) {
-#pragma unroll
       for (int gg = 0; gg < NG; ++gg) {
-        const float e = m_s[gg] == kNegInf ? 0.f : fast_exp2(m_s[gg] - M);
-        tot += acc_s[gg][t] * e;
-        dt += den_s[gg] * e;
+        const float mg = m_s[gg * NI + t];
+        const float e = mg == kNegInf ? 0.f : fast_exp2(mg - M);
+        tot += acc_s[gg * NI + t] * e;
+        dt += den_s[gg * NI + t] * e;
       }
     }
+    const int64_t row = ((int64_t)b * Q + rr / G) * Hq + g * G + rr % G;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      store_out(a.out, (OutT)a.out_dtype, row * D + 4 * t + r, dt > 0.f ? tot[r] / dt : 0.f);
+      store_out(a.out, (OutT)a.out_dtype, row * D + 4 * c + r, dt > 0.f ? tot[r] / dt : 0.f);
   }
 }
 
@@ -1808,8 +1810,9 @@ static hipError_t launch_flat(const AttnArgs& a, hipStream_t stream) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const unsigned out_rows = (unsigned)((int64_t)a.batch * a.q_len * a.num_q_heads);
-    hipLaunchKernelGGL((attn_flat_merge_kernel<D>), dim3(out_rows), dim3(256), 0, stream, a);
+    const unsigned pairs = (unsigned)((int64_t)a.batch * a.num_kv_heads);   // (sequence, KV head)
+    hipLaunchKernelGGL((attn_flat_merge_kernel<D>), dim3(pairs), dim3(kFlatMergeThreads), 0,
+                       stream, a);
     return hipGetLastError();
   }
 }
