@@ -1026,12 +1026,15 @@ void attn_partition_kernel(const AttnArgs a) {
 
 // Built for three waves per SIMD in the 4-row form (up to 168 registers) and
 // two in the 16-row form, which holds more per lane.
+// wavefronts per workgroup of the balanced kernel, by tile rows
+template <int RT> constexpr int kFlatWaves = RT == 4 ? 8 : 4;
+
 template <Fmt KV, int D, int RT, int HP>
-__global__ __launch_bounds__((Shape<KV, RT>::NW * kWave), (RT == 4 ? 3 : 2))
+__global__ __launch_bounds__((kFlatWaves<RT> * kWave), (RT == 4 ? 3 : 2))
 void attn_flat_kernel(const AttnArgs a) {
   using MM = Mma<KV>;
   static_assert(KV != Fmt::K8V4, "balanced split: 16-bit caches");
-  constexpr int NW = Shape<KV, RT>::NW;
+  constexpr int NW = kFlatWaves<RT>;
   constexpr int NWH = NW / HP;
   constexpr int KS = D / 32, NT = D / 16;
   constexpr int QSTR = D + 8;
@@ -1794,14 +1797,14 @@ static hipError_t launch_flat(const AttnArgs& a, hipStream_t stream) {
     const int rows = a.gqa * a.q_len;
     const int hp = a.num_kv_heads % 2 == 0 ? 2 : 1;
     if (rows <= 4) {
-      constexpr int NW = Shape<KV, 4>::NW;
+      constexpr int NW = kFlatWaves<4>;
       const dim3 grid((unsigned)(a.flat_runs / (NW / hp)), (unsigned)(a.num_kv_heads / hp));
       if (hp == 2)
         hipLaunchKernelGGL((attn_flat_kernel<KV, D, 4, 2>), grid, dim3(NW * kWave), 0, stream, a);
       else
         hipLaunchKernelGGL((attn_flat_kernel<KV, D, 4, 1>), grid, dim3(NW * kWave), 0, stream, a);
     } else {
-      constexpr int NW = Shape<KV, 16>::NW;
+      constexpr int NW = kFlatWaves<16>;
       const dim3 grid((unsigned)(a.flat_runs / (NW / hp)), (unsigned)(a.num_kv_heads / hp));
       if (hp == 2)
         hipLaunchKernelGGL((attn_flat_kernel<KV, D, 16, 2>), grid, dim3(NW * kWave), 0, stream, a);
