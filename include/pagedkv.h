@@ -376,6 +376,12 @@ int paged_attention_decode_cascade(void* out, int out_dtype, const void* query,
  * number of (block, KV head, token) V rows read.  Same arguments, workspace
  * and errors as paged_attention_decode_splitkv otherwise; v_threshold outside
  * [0, 1) is PKV_ERR_SHAPE; needs gqa_factor * q_len <= 4 and a 16-bit cache.
+ * Not recommended on MI355X: the dense split-KV call is faster even where
+ * this one reads a tenth of the V rows (32K context, sharply peaked rows:
+ * 69 against 32.5 us per layer), because the K -> V dependency adds a
+ * workgroup barrier and an exposed V load per round while the dense kernel
+ * is bound by load structure and latency, not by bytes.  It is kept as the
+ * reading of the pages' traffic deletion, with its proven error bound.
  */
 int paged_attention_decode_splitkv_sparse_v(
     void* out, int out_dtype, const void* query, const void* key_cache, const void* value_cache,
