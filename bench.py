@@ -59,6 +59,9 @@ def parse():
                          "next to the partition kernel")
     ap.add_argument("--only", default=None,
                     help="time only this one of the other workloads (for profiling), e.g. k8v4")
+    ap.add_argument("--only-partition", default=None,
+                    help="with --only: the split to time instead of the workload's own "
+                         "(direct, 0 for the balanced split, or a partition size)")
     return ap.parse_args()
 
 
@@ -681,8 +684,13 @@ def main():
         if args.only not in runners:
             print(json.dumps({"error": f"unknown workload {args.only}; one of {sorted(runners)}"}))
             sys.exit(2)
+        if args.only_partition is not None and args.only in OTHER:
+            seed, layers, _ = OTHER[args.only]
+            part = None if args.only_partition == "direct" else int(args.only_partition)
+            OTHER[args.only] = (seed, layers, part)
         log(f"timing {args.only}")
-        print(json.dumps({"workload": args.only, **runners[args.only]()}), flush=True)
+        print(json.dumps({"workload": args.only, "library": os.path.basename(P.lib._name),
+                          **runners[args.only]()}), flush=True)
         return
 
     log("building the 32K workload")
@@ -715,6 +723,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
+        "library": os.path.basename(P.lib._name),
         "config": {
             "workload": "long32k: single-user split-KV decode, batch 1, q_len 1, 32 query / 8 KV "
                         "heads, head_dim 128, fp16 K/V, context 32768 (2048 blocks of 16, "

@@ -13,7 +13,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libpagedkv.so")
+# PKV_LIBRARY names another build of the same ABI (the measurement variant
+# libpagedkv_qkvalu.so, for an A/B); by default the product library
+LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(PKG, "libpagedkv.so")
 
 PKV_F16, PKV_BF16, PKV_F32 = 0, 1, 2
 PKV_FMT_F16, PKV_FMT_BF16, PKV_FMT_K8V4 = 0, 1, 3

@@ -22,6 +22,9 @@ SOURCES = ["api.hip", "write_kernels.hip", "attn_kernels.hip", "gather_kernels.h
 # read-only measurement probes (pagedkv_probe.h), a library of their own
 PROBE_LIB = os.path.join(PKG, "libpagedkv_probe.so")
 PROBE_SOURCES = ["probe_kernels.hip"]
+# measurement variant: the 16-bit partition kernel's scores on vector dot
+# products instead of MFMA (same ABI; loaded with PKV_LIBRARY for an A/B)
+QKVALU_LIB = os.path.join(PKG, "libpagedkv_qkvalu.so")
 ARCH = "gfx950"
 
 
@@ -43,19 +46,23 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     decode library and the probe library."""
     _build_lib(SOURCES, LIB, verbose, jobs)
     _build_lib(PROBE_SOURCES, PROBE_LIB, verbose, jobs)
+    _build_lib(SOURCES, QKVALU_LIB, verbose, jobs, defines={"attn_kernels.hip": ["-DPKV_QK_VALU=1"]},
+               tag="qkvalu")
     return LIB
 
 
-def _build_lib(sources, lib, verbose, jobs):
+def _build_lib(sources, lib, verbose, jobs, defines=None, tag=""):
     cc = hipcc()
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
     procs = []
     objs = []
     for src in sources:
-        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        extra = (defines or {}).get(src, [])
+        stem = src.replace(".hip", "") + ("_" + tag if extra else "")
+        obj = os.path.join(objdir, stem + ".o")
         objs.append(obj)
-        cmd = [cc, *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

@@ -68,9 +68,17 @@
 #include "pkv_common.h"
 #include "pkv_launch.h"
 
+// PKV_QK_VALU=1 builds a measurement variant of the library in which the
+// 16-bit partition kernel computes the scores with vector dot products
+// instead of MFMA (libpagedkv_qkvalu.so; the MFMA build is the product).
+#ifndef PKV_QK_VALU
+#define PKV_QK_VALU 0
+#endif
+
 namespace pkv {
 
 constexpr float kNegInf = -INFINITY;
+constexpr bool kQkOnValu = PKV_QK_VALU != 0;
 
 // Head dims of the K/Q operand held by quarter qd at QK step m (8 consecutive).
 template <Fmt KV>
@@ -261,7 +269,9 @@ struct AttnSmem {
   static constexpr int GR = D / 32;                        // V groups per row
   static constexpr int VT = 16 * D * 2;                    // one staged V tile (bytes)
   static constexpr int VST = NW * VT;
-  static constexpr int SIDE = KV == Fmt::K8V4 ? NW * 16 * (1 + 2 * GR) * 4 : 0;
+  // K8/V4: per-token scales; the vector-dot score variant: per-wave scores
+  static constexpr int SIDE = KV == Fmt::K8V4 ? NW * 16 * (1 + 2 * GR) * 4
+                              : kQkOnValu ? NW * RT * 16 * 4 : 0;
   static constexpr int EP = RT == 16 ? 2 : 1;              // merge passes over the head dims
   static constexpr int MO = NW * RT * (D / EP) * 4;        // merge: per-wave outputs (one pass)
   static constexpr int LOOP = VST + SIDE;
@@ -794,6 +804,46 @@ void attn_partition_kernel(const AttnArgs a) {
           side[16 + rho * 2 * GR + 2 * gi + 1] = tok_ok ? zv : 0.f;
         }
       }
+    } else if constexpr (kQkOnValu) {
+      // vector dot products: lane (rho, qd) dots token rho's dims
+      // 32 m + 8 qd .. +7 with the same dims of every tile row c, the four
+      // quarters are summed with lane swaps, and the scores pass through LDS
+      // into the layout the MFMA produces (lane l: row l % 16, tokens
+      // 4 (l / 16) + r)
+      float* scs = (float*)(smem + SM::VST) + w * RT * 16;
+      float part[RT];
+#pragma unroll
+      for (int c = 0; c < RT; ++c) part[c] = 0.f;
+#pragma unroll
+      for (int m = 0; m < KS; ++m) {
+        const uint32_t kw[4] = {br.k[m].x, br.k[m].y, br.k[m].z, br.k[m].w};
+#pragma unroll
+        for (int c = 0; c < RT; ++c) {
+          if (c >= GQT) continue;                              // wave-uniform
+          const u4 q4 = *(const u4*)(qw + c * QSTR + qk_dim<KV>(m, qd));
+          const uint32_t qv4[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (QT == Fmt::F16)
+              part[c] = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, kw[e]),
+                                               __builtin_bit_cast(h2, qv4[e]), part[c], false);
+            else {
+              typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+              part[c] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, kw[e]),
+                                                        __builtin_bit_cast(bf2, qv4[e]), part[c],
+                                                        false);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < RT; ++c) {
+        if (c >= GQT) continue;
+        const float tot = quarter_sum(part[c]);
+        if (qd == 0) scs[c * 16 + rho] = tot;
+      }
+      wave_lds_fence();
+      s = s + *(const f4*)(scs + (row_ok ? lrow : lrow % GQ) * 16 + 4 * qd);
     } else {
 #pragma unroll
       for (int m = 0; m < KS; ++m) {
