@@ -300,7 +300,7 @@ OTHER = {
     "tiny": (1, 32, None),
     "llama8b_batch": (2, 32, 0),
     "spec_verify": (4, 32, 0),
-    "k8v4": (5, 32, 2048),
+    "k8v4": (5, 32, 512),
     "long32k_window2048": (3, 32, 128),
 }
 WINDOW = {"long32k_window2048": 2048}       # sliding window of the windowed workloads

@@ -257,15 +257,17 @@ __device__ __forceinline__ void load_block(const AttnArgs& a, int64_t pb, bool l
 // (the 16-row form's LDS, merge included, stays under 40 KB so that four
 // workgroups share a CU), and the K8/V4 16-row form, which holds more per
 // lane, 4 wavefronts at 3.
-template <Fmt KV, int RT> struct Shape {
+// The K8/V4 head-group form (HP KV heads per workgroup) runs one wavefront
+// per head.
+template <Fmt KV, int RT, int HP = 1> struct Shape {
   static constexpr bool WIDE = RT == 4 && KV != Fmt::K8V4;
-  static constexpr int NW = WIDE ? 8 : 4;
+  static constexpr int NW = KV == Fmt::K8V4 && HP > 1 ? HP : WIDE ? 8 : 4;
   static constexpr int WAVES_PER_SIMD = RT == 4 || KV != Fmt::K8V4 ? 4 : 3;
 };
 
-template <Fmt KV, int D, int RT>
+template <Fmt KV, int D, int RT, int HP = 1>
 struct AttnSmem {
-  static constexpr int NW = Shape<KV, RT>::NW;
+  static constexpr int NW = Shape<KV, RT, HP>::NW;
   static constexpr int GR = D / 32;                        // V groups per row
   static constexpr int VT = 16 * D * 2;                    // one staged V tile (bytes)
   static constexpr int VST = NW * VT;
@@ -282,8 +284,8 @@ struct AttnSmem {
   static constexpr int BYTES_APPEND = LOOP + STASH > MO ? LOOP + STASH : MO;
   // forms with HP > 1 heads per workgroup: a parked tile per head, and more
   // than half of a CU's 160 KB, so that one workgroup runs per CU
-  template <int HP> static constexpr int bytes_group() {
-    constexpr int used = LOOP + HP * STASH > MO ? LOOP + HP * STASH : MO;
+  template <int NH> static constexpr int bytes_group() {
+    constexpr int used = LOOP + NH * STASH > MO ? LOOP + NH * STASH : MO;
     return used > 82 * 1024 ? used : 82 * 1024;
   }
   static constexpr int QSTR = D + 8;                       // halves per staged query row
@@ -327,16 +329,24 @@ constexpr float kRescaleSlack = 8.f;
 // partition; a token row's HP heads (HP * 256 contiguous bytes at D = 128)
 // are then read together, and one workgroup runs per CU.
 // (The grouped forms run one workgroup per CU, so two waves per SIMD.)
+//
+// K8/V4 head groups (HP = 8): one wavefront per KV head, each walking the
+// whole partition, so a block's K and V rows of all heads (a 1 KiB K row and
+// a 512-byte V row per token at D = 128) and its scale lines are read by one
+// CU at once, and no merge inside the workgroup is needed; chosen when the
+// grid of head groups fills every CU at least once.
 template <Fmt KV, Fmt QT, int D, int RT, bool PREFIX, int HP = 1>
-__global__ __launch_bounds__((Shape<KV, RT>::NW * kWave),
-                             (HP > 1 ? Shape<KV, RT>::NW / 4 : Shape<KV, RT>::WAVES_PER_SIMD))
+__global__ __launch_bounds__((Shape<KV, RT, HP>::NW * kWave),
+                             (HP > 1 ? Shape<KV, RT, HP>::NW / 4 : Shape<KV, RT>::WAVES_PER_SIMD))
 void attn_partition_kernel(const AttnArgs a) {
   using MM = Mma<QT>;
-  using SM = AttnSmem<KV, D, RT>;
+  using SM = AttnSmem<KV, D, RT, HP>;
   constexpr int NW = SM::NW;
   constexpr int NWH = NW / HP;         // waves per head
-  static_assert(HP == 1 || ((HP == 2 || HP == 4) && !PREFIX && KV != Fmt::K8V4 && RT == 4),
-                "head pairs: 16-bit caches, 4-row tiles, plain mode");
+  static_assert(HP == 1 || ((HP == 2 || HP == 4) && !PREFIX && KV != Fmt::K8V4 && RT == 4) ||
+                    (HP == 8 && !PREFIX && KV == Fmt::K8V4 && RT == 4),
+                "head groups: 16-bit caches in pairs or quads, K8/V4 in eights; 4-row tiles, "
+                "plain mode");
   constexpr int KS = D / 32;           // QK MFMA steps
   constexpr int NT = D / 16;           // PV output tiles
   constexpr int GR = SM::GR;
@@ -364,7 +374,7 @@ void attn_partition_kernel(const AttnArgs a) {
   // 8 * (g + Hkv * (u / 8)) + u % 8 is head g of unit u = p + parts * b; the
   // grid is rounded up to whole groups of eight units.
   int p, g, b;
-  if constexpr (KV == Fmt::K8V4) {
+  if constexpr (KV == Fmt::K8V4 && HP == 1) {
     const int id = (int)blockIdx.x, hk = a.num_kv_heads;
     const int u = (id / (8 * hk)) * 8 + (id & 7);
     if (u >= a.num_parts * a.batch) return;                 // past the last unit (whole group)
@@ -1880,6 +1890,19 @@ static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream, int stage)
     const int rows = (a.mode == 1 ? a.group_size : 1) * a.gqa * a.q_len;
     dim3 grid((unsigned)a.num_parts, (unsigned)a.num_kv_heads,
               (unsigned)(a.mode == 1 ? a.num_groups : a.batch));
+    if constexpr (KV == Fmt::K8V4) {
+      // head groups of eight when their grid fills every CU at least once
+      const int64_t hg_wgs = (int64_t)a.num_parts * (a.num_kv_heads / 8) * a.batch;
+      const int64_t cus = device_cu_count();
+      if (a.mode == 0 && rows <= 4 && a.num_kv_heads % 8 == 0 && cus > 0 && hg_wgs >= cus) {
+        const dim3 hgrid((unsigned)a.num_parts, (unsigned)(a.num_kv_heads / 8), (unsigned)a.batch);
+        hipLaunchKernelGGL((attn_partition_kernel<KV, QT, D, 4, false, 8>), hgrid,
+                           dim3(Shape<KV, 4, 8>::NW * kWave), 0, stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || a.ws_o == nullptr || stage == STAGE_PARTIALS) return e;
+        return launch_merge<D>(a, stream);
+      }
+    }
     if constexpr (KV == Fmt::K8V4) {     // 1-D, XCD-grouped order (see the kernel)
       if (a.mode != 0) return hipErrorInvalidValue;
       const int64_t units = (int64_t)a.num_parts * a.batch;

@@ -199,3 +199,57 @@ def test_k8v4_few_query_rows_append(P, name, split, psize):
     assert_k8v4_arrays_equal(arrs, after)
     err = max_err(out, ref)
     assert err <= 2e-4, f"{name}: fp32-out max abs err {err}"
+
+
+# ------------------------------------------------------------------ K8/V4 head groups
+#
+# With eight KV heads and at least one workgroup of eight heads per CU
+# (partitions x sequences >= 256 here), the K8/V4 kernel runs one wavefront per
+# head, each over its whole partition, eight heads per workgroup.
+
+K8_HEAD_GROUPS = {
+    # 10 partitions of 32 tokens x 40 sequences = 400 head-group workgroups
+    "hg_b40_p32": (lambda: small(160, batch=40, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                                 lengths=lambda r: r.integers(200, 320, size=40)), 32),
+    "hg_g1_d64_p16": (lambda: small(161, batch=48, num_q_heads=8, num_kv_heads=8, head_dim=64,
+                                    fmt="bf16", lengths=lambda r: r.integers(1, 150, size=48)), 16),
+    "hg_q2_g2_p64": (lambda: small(162, batch=36, q_len=2, num_q_heads=16, num_kv_heads=8,
+                                   head_dim=128, lengths=lambda r: r.integers(2, 600, size=36)), 64),
+    # the K8/V4 batch at partition 512: 16 x 16 = 256 workgroups
+    "k8v4_p512": (lambda: W.k8v4(), 512),
+}
+_hg = {}
+
+
+def hg_case(name):
+    if name not in _hg:
+        _hg.clear()
+        case = K8_HEAD_GROUPS[name][0]()
+        arrs = oracle_k8v4_pool(case)[0]
+        ref = oracle.paged_attention_k8v4(case.query, case.fmt, *arrs, case.block_tables,
+                                          case.context_lens, case.scale, case.gqa_factor)
+        _hg[name] = (case, arrs, ref, k8v4_append_expected(case))
+    return _hg[name]
+
+
+@pytest.mark.parametrize("name", list(K8_HEAD_GROUPS))
+def test_k8v4_head_groups(P, name):
+    case, arrs, ref, (before, after, aref) = hg_case(name)
+    psize = K8_HEAD_GROUPS[name][1]
+    print(f"[k8v4 head groups] {name} partition {psize}", flush=True)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()      # noqa: E731
+    q = bits_to_dev(case.query, case.fmt)
+    mcl = int(case.context_lens.max())
+    n = P.splitkv_workspace_size(*q.shape[:3], q.shape[3], mcl, psize)
+    ws = torch.full((n // 4 + 4,), float("nan"), dtype=torch.float32, device="cuda")
+    out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    P.paged_attention_decode_splitkv_k8v4(out, q, *[dev(a) for a in arrs], dev(case.block_tables),
+                                          dev(case.context_lens), case.scale, case.gqa_factor,
+                                          mcl, psize, ws)
+    torch.cuda.synchronize()
+    err = max_err(out, ref)
+    assert err <= 2e-4, f"{name}: fp32-out max abs err {err}"
+    out2, got = run_k8v4_append(P, case, before, split=True, psize=psize)
+    assert_k8v4_arrays_equal(got, after)
+    err = max_err(out2, aref)
+    assert err <= 2e-4, f"{name} append: fp32-out max abs err {err}"

@@ -672,11 +672,13 @@ def test_k8v4_append_matches_quantize_then_attend(P, name, split, psize):
     assert torch.equal(out16, out.to(tdtype(case.fmt)))
 
 
-def test_k8v4_append_batch_launch_configuration(P):
+@pytest.mark.parametrize("psize", [512, 2048])
+def test_k8v4_append_batch_launch_configuration(P, psize):
     """The K8/V4 batch step as the bench times it: 16 x 8192 tokens, split-KV
-    partition 2048, fp16 output."""
+    partition 512 (eight-head workgroups), fp16 output; and at 2048, the
+    one-head form it was timed at before."""
     case, before, after, ref = get_k8v4_append_case("k8v4")
-    out, arrs = run_k8v4_append(P, case, before, split=True, psize=2048, out_dtype=torch.float16)
+    out, arrs = run_k8v4_append(P, case, before, split=True, psize=psize, out_dtype=torch.float16)
     assert_k8v4_arrays_equal(arrs, after)
     assert max_err(out, ref) <= TOL
 
