@@ -1855,18 +1855,26 @@ static hipError_t launch_flat(const AttnArgs& a, hipStream_t stream) {
     return hipErrorInvalidValue;
   } else {
     const int rows = a.gqa * a.q_len;
-    const int hp = a.num_kv_heads % 2 == 0 ? 2 : 1;
+    // heads per workgroup: all of a workgroup's waves on one run, one head
+    // each (a block's token rows of all those heads read by one CU), when the
+    // KV heads divide into groups of that size; else pairs, else one head
     if (rows <= 4) {
       constexpr int NW = kFlatWaves<4>;
+      const int hp = a.num_kv_heads % NW == 0 ? NW : a.num_kv_heads % 2 == 0 ? 2 : 1;
       const dim3 grid((unsigned)(a.flat_runs / (NW / hp)), (unsigned)(a.num_kv_heads / hp));
-      if (hp == 2)
+      if (hp == NW)
+        hipLaunchKernelGGL((attn_flat_kernel<KV, D, 4, NW>), grid, dim3(NW * kWave), 0, stream, a);
+      else if (hp == 2)
         hipLaunchKernelGGL((attn_flat_kernel<KV, D, 4, 2>), grid, dim3(NW * kWave), 0, stream, a);
       else
         hipLaunchKernelGGL((attn_flat_kernel<KV, D, 4, 1>), grid, dim3(NW * kWave), 0, stream, a);
     } else {
       constexpr int NW = kFlatWaves<16>;
+      const int hp = a.num_kv_heads % NW == 0 ? NW : a.num_kv_heads % 2 == 0 ? 2 : 1;
       const dim3 grid((unsigned)(a.flat_runs / (NW / hp)), (unsigned)(a.num_kv_heads / hp));
-      if (hp == 2)
+      if (hp == NW)
+        hipLaunchKernelGGL((attn_flat_kernel<KV, D, 16, NW>), grid, dim3(NW * kWave), 0, stream, a);
+      else if (hp == 2)
         hipLaunchKernelGGL((attn_flat_kernel<KV, D, 16, 2>), grid, dim3(NW * kWave), 0, stream, a);
       else
         hipLaunchKernelGGL((attn_flat_kernel<KV, D, 16, 1>), grid, dim3(NW * kWave), 0, stream, a);
