@@ -161,6 +161,29 @@ class Long32K:
         return s, e
 
 
+def long32k_other_partition(wl, P, torch, part, steps, warmup):
+    """The headline step (append form, same 32 layer caches) at another
+    partition size; reported beside the headline, which keeps 512."""
+    c = wl.case
+    n = P.splitkv_workspace_size(1, 1, wl.hq, wl.d, wl.L, part)
+    ws = torch.zeros(n // 4 + 4, dtype=torch.float32, device="cuda")
+
+    def step():
+        for l in range(wl.layers):
+            P.paged_attention_decode_splitkv_append(wl.out[l], wl.q[l], wl.nk[l], wl.nv[l], wl.K[l],
+                                                    wl.V[l], wl.bt, wl.cl, c.scale, c.gqa_factor,
+                                                    wl.L, part, ws)
+    ms, med = time_steps(torch, graph_of(torch, step).replay, steps, warmup, median=True)
+    us = ms * 1e3 / wl.layers
+    return {"us_per_layer": round(us, 3), "median_us_per_layer": round(med * 1e3 / wl.layers, 3),
+            "kv_bytes_per_layer": wl.layer_bytes,
+            "kv_stream_gbs": round(wl.layer_bytes / (us * 1e-6) / 1e9, 2),
+            "pct_of_hbm_peak": round(100 * wl.layer_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+            "layers": wl.layers, "partition_size": part,
+            "form": f"split-KV partition {part} (eight KV heads per workgroup, one wave per head), "
+                    "append form, HIP graph; finer partials than the 512-token headline"}
+
+
 def graph_of(torch, fn):
     """Capture one call of ``fn`` (a whole step's launches, stream-ordered on
     the current stream) into a HIP graph.  Nothing is allocated or cleared by
@@ -756,9 +779,11 @@ def main():
         },
     }
     if not args.no_extra:
+        log("timing long32k at 128-token partitions")
+        finer = long32k_other_partition(wl, P, torch, 128, args.steps, args.warmup)
         del wl.K, wl.V
         torch.cuda.empty_cache()
-        result["other_workloads"] = {}
+        result["other_workloads"] = {"long32k_partition128": finer}
         for name in ("tiny", "llama8b_batch", "spec_verify", "k8v4", "long32k_window2048"):
             log(f"timing {name}")
             result["other_workloads"][name] = other_workload(name, P, W, torch, args.steps,

@@ -324,10 +324,11 @@ __device__ __forceinline__ u2 lds_read_tr16(const unsigned char* p) {
 constexpr float kRescaleSlack = 8.f;
 
 // HP: KV heads per workgroup.  1: the workgroup's NW waves share one head and
-// split its partition into runs.  2 or 4 (16-bit caches, plain mode): waves
+// split its partition into runs.  2, 4 or 8 (16-bit caches, plain mode): waves
 // hw*NW/HP .. take head HP*blockIdx.y + hw, each group splitting the same
-// partition; a token row's HP heads (HP * 256 contiguous bytes at D = 128)
-// are then read together, and one workgroup runs per CU.
+// partition (with 8, one wave per head walks the whole partition); a token
+// row's HP heads (HP * 256 contiguous bytes at D = 128) are then read
+// together, and one workgroup runs per CU.
 // (The grouped forms run one workgroup per CU, so two waves per SIMD.)
 //
 // K8/V4 head groups (HP = 8): one wavefront per KV head, each walking the
@@ -343,10 +344,10 @@ void attn_partition_kernel(const AttnArgs a) {
   using SM = AttnSmem<KV, D, RT, HP>;
   constexpr int NW = SM::NW;
   constexpr int NWH = NW / HP;         // waves per head
-  static_assert(HP == 1 || ((HP == 2 || HP == 4) && !PREFIX && KV != Fmt::K8V4 && RT == 4) ||
-                    (HP == 8 && !PREFIX && KV == Fmt::K8V4 && RT == 4),
-                "head groups: 16-bit caches in pairs or quads, K8/V4 in eights; 4-row tiles, "
-                "plain mode");
+  static_assert(HP == 1 || ((HP == 2 || HP == 4 || HP == 8) && !PREFIX && RT == 4 &&
+                            (KV != Fmt::K8V4 || HP == 8)),
+                "head groups: 16-bit caches in pairs, quads or eights, K8/V4 in eights; "
+                "4-row tiles, plain mode");
   constexpr int KS = D / 32;           // QK MFMA steps
   constexpr int NT = D / 16;           // PV output tiles
   constexpr int GR = SM::GR;
@@ -1748,25 +1749,35 @@ hipError_t launch_sparse_v(const AttnArgs& a, int kv_fmt, int head_dim, hipStrea
   return launch_attention(a, kv_fmt, kv_fmt, head_dim, stream, STAGE_MERGE);
 }
 
-// Log-sum-exp merge of the split-KV partials: one workgroup per output row
-// (b, i, h).  out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, M = max_p m_p.
+// Log-sum-exp merge of the split-KV partials: one workgroup per DC output
+// dims of an output row (b, i, h), grid (rows, D / DC).
+// out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, M = max_p m_p.
 // Single pass: thread (c, grp) takes partitions grp, grp+NG, ... for the 4
 // dims of chunk c, folding each into a running (max, sum, acc) so every load
-// can be in flight at once; the NG running states are then combined in LDS.
-template <int D>
+// can be in flight at once.  The NG running states are then combined in
+// parallel: the workgroup's max M, every state rescaled to M by its own
+// thread, and a sum over the groups (xor shuffles inside a wavefront, the
+// four wavefronts' sums in LDS).  DC < D is for few rows: more workgroups,
+// each with fewer partitions per thread, so that one round of loads covers
+// many partitions.
+template <int D, int DC>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
-  constexpr int NC = D / 4;              // float4 chunks per row
+  static_assert(D % DC == 0 && DC % 4 == 0 && DC / 4 <= kWave && (DC / 4 & (DC / 4 - 1)) == 0,
+                "merge slice: a power-of-two count of float4 chunks, at most a wavefront");
+  constexpr int NC = DC / 4;             // float4 chunks per workgroup
   constexpr int NG = 256 / NC;           // partition groups
-  __shared__ f4 acc_s[NG][NC];
-  __shared__ float m_s[NG], den_s[NG];
+  constexpr int NWV = 256 / kWave;       // wavefronts
+  __shared__ f4 acc_s[NWV][NC];
+  __shared__ float m_s[NWV], den_s[NWV];
 
   const int64_t row = blockIdx.x;
+  const int col0 = blockIdx.y * DC;
   const int t = threadIdx.x;
   // every partition of the grid holds a partial or an empty marker (max -inf)
   const int np = a.ws_parts;
   const float* wm = a.ws_m + row * np;
   const float* wl = a.ws_l + row * np;
-  const float* wo = a.ws_o + row * np * D;
+  const float* wo = a.ws_o + row * np * D + col0;
 
   const int c = t % NC, grp = t / NC;
   float m_t = kNegInf, den = 0.f;
@@ -1802,36 +1813,59 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnArgs a) {
       m_t = m_new;
     }
   }
-  acc_s[grp][c] = acc;
-  if (c == 0) {
-    m_s[grp] = m_t;
-    den_s[grp] = den;
+  // lanes c, c + NC, ... of a wavefront hold the same chunk of different groups
+  const int lane = t % kWave, w = t / kWave;
+  float mx = m_t;
+#pragma unroll
+  for (int d = NC; d < kWave; d <<= 1) mx = fmaxf(mx, __shfl_xor(mx, d, kWave));
+  if (lane == 0) m_s[w] = mx;
+  __syncthreads();
+  float M = m_s[0];
+#pragma unroll
+  for (int i = 1; i < NWV; ++i) M = fmaxf(M, m_s[i]);
+  // a group that saw nothing (and with it M -inf, when no partition saw
+  // anything) weighs 0
+  const float e = m_t == kNegInf ? 0.f : fast_exp2(m_t - M);
+  acc = acc * e;
+  den = den * e;
+#pragma unroll
+  for (int d = NC; d < kWave; d <<= 1) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] += __shfl_xor(acc[r], d, kWave);
+    den += __shfl_xor(den, d, kWave);
   }
+  if (lane < NC) acc_s[w][lane] = acc;
+  if (lane == 0) den_s[w] = den;
   __syncthreads();
   if (t < NC) {
-    float M = kNegInf;
+    f4 tot = acc_s[0][t];
+    float dt = den_s[0];
 #pragma unroll
-    for (int gg = 0; gg < NG; ++gg) M = fmaxf(M, m_s[gg]);
-    f4 tot = f4{0.f, 0.f, 0.f, 0.f};
-    float dt = 0.f;
-    if (M != kNegInf) {
-#pragma unroll
-      for (int gg = 0; gg < NG; ++gg) {
-        const float e = m_s[gg] == kNegInf ? 0.f : fast_exp2(m_s[gg] - M);
-        tot += acc_s[gg][t] * e;
-        dt += den_s[gg] * e;
-      }
+    for (int i = 1; i < NWV; ++i) {
+      tot += acc_s[i][t];
+      dt += den_s[i];
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      store_out(a.out, (OutT)a.out_dtype, row * D + 4 * t + r, dt > 0.f ? tot[r] / dt : 0.f);
+      store_out(a.out, (OutT)a.out_dtype, row * D + col0 + 4 * t + r,
+                dt > 0.f ? tot[r] / dt : 0.f);
   }
 }
+
+static int device_cu_count();
 
 template <int D>
 static hipError_t launch_merge(const AttnArgs& a, hipStream_t stream) {
   const unsigned rows = (unsigned)((int64_t)a.batch * a.q_len * a.num_q_heads);
-  hipLaunchKernelGGL((attn_merge_kernel<D>), dim3(rows), dim3(256), 0, stream, a);
+  // a whole-row workgroup loads 8 partitions per thread in one round; with
+  // more partitions than that and rows too few to fill the compute units,
+  // 32-dim slices keep it to one round (and spread it over more CUs)
+  constexpr int kOneRound = 8 * (256 / (D / 4));
+  const int cus = device_cu_count();
+  if (a.ws_parts > kOneRound && cus > 0 && (int64_t)rows <= 2 * (int64_t)cus)
+    hipLaunchKernelGGL((attn_merge_kernel<D, 32>), dim3(rows, D / 32), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((attn_merge_kernel<D, D>), dim3(rows), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -1945,6 +1979,7 @@ static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream, int stage)
       if (rows <= 4 && a.mode == 0 && cus > 0 && wgs > cus) {
         if (a.num_kv_heads % 2 == 0 && wgs <= 2 * cus) hp = 2;
         else if (a.num_kv_heads % 4 == 0 && wgs <= 4 * cus) hp = 4;
+        else if (a.num_kv_heads % 8 == 0 && wgs <= 8 * cus) hp = 8;   // one wave per head
       }
     }
     if (hp > 1) {
@@ -1953,8 +1988,11 @@ static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream, int stage)
         if (hp == 2)
           hipLaunchKernelGGL((attn_partition_kernel<KV, QT, D, 4, false, 2>), hgrid,
                              dim3(Shape<KV, 4>::NW * kWave), 0, stream, a);
-        else
+        else if (hp == 4)
           hipLaunchKernelGGL((attn_partition_kernel<KV, QT, D, 4, false, 4>), hgrid,
+                             dim3(Shape<KV, 4>::NW * kWave), 0, stream, a);
+        else
+          hipLaunchKernelGGL((attn_partition_kernel<KV, QT, D, 4, false, 8>), hgrid,
                              dim3(Shape<KV, 4>::NW * kWave), 0, stream, a);
       }
     } else if (rows <= 4) {

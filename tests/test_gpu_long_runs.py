@@ -9,8 +9,9 @@ direct form and at 12288- and 16384-token partitions), head pairs and head
 quads (batches sized so that the one-head grid needs two, or up to four,
 workgroups per CU of a 256-CU device), in the decode, append, window and
 windowed-append calls, each against the oracle.  The spec-verify commit runs
-at the workload's full size, and the K8/V4 column-group tiles run with
-G * q_len of 1, 2 and 3 (copy columns past the real rows).
+at the workload's full size, the K8/V4 column-group tiles run with
+G * q_len of 1, 2 and 3 (copy columns past the real rows), and the merge of
+the partials runs in both of its forms (whole rows, 32-dim slices).
 """
 
 import numpy as np
@@ -253,3 +254,77 @@ def test_k8v4_head_groups(P, name):
     assert_k8v4_arrays_equal(got, after)
     err = max_err(out2, aref)
     assert err <= 2e-4, f"{name} append: fp32-out max abs err {err}"
+
+
+# ------------------------------------------------------------------ 16-bit eight-head groups
+#
+# When the one-head grid needs four to eight workgroups per CU (of 256) and the
+# KV heads divide by eight, the 16-bit kernel runs eight heads per workgroup,
+# one wavefront per head over its whole partition.
+
+EIGHTS = {
+    # 32K at 128-token partitions: 256 x 8 = 2048 one-head workgroups
+    "long32k_p128": (lambda: W.long32k(), 128, 2000),
+    # 10 partitions of 32 tokens x 8 heads x 20 sequences = 1600
+    "eights_b20_p32": (lambda: small(163, batch=20, q_len=1, num_q_heads=32, num_kv_heads=8,
+                                     head_dim=128, fmt="bf16",
+                                     lengths=lambda r: r.integers(200, 320, size=20)), 32, 100),
+    "eights_q2_d64_p32": (lambda: small(164, batch=14, q_len=2, num_q_heads=16, num_kv_heads=8,
+                                        head_dim=64, lengths=lambda r: r.integers(2, 300, size=14)),
+                          32, 40),
+}
+
+
+@pytest.mark.parametrize("name", list(EIGHTS))
+def test_eight_head_groups(P, name):
+    builder, psize, window = EIGHTS[name]
+    case = builder()
+    dc = DevCase(case)
+    for kind in ("decode", "append", "window_append"):
+        print(f"[eights] {name} {kind} partition {psize}", flush=True)
+        ref, kc, vc = _reference(case, kind, window)
+        if kind == "decode":
+            out = run_decode(P, dc, split=True, partition_size=psize)
+        elif kind == "append":
+            out, k, v = run_append(P, dc, split=True, psize=psize)
+        else:
+            out, k, v = run_window_append(P, dc, window, split=True, psize=psize)
+        if kind != "decode":
+            assert np.array_equal(dev_to_bits(k), kc) and np.array_equal(dev_to_bits(v), vc)
+        err = max_err(out, ref)
+        assert err <= 2e-4, f"{name} {kind}: fp32-out max abs err {err}"
+
+
+# The merge of the split partials: with few output rows (at most two per
+# compute unit) each row is taken by D / 32 workgroups of 32 dims, else by one
+# workgroup that loops over rounds of loads when the partitions are many.
+MERGES = {
+    # 188 partitions, 8 rows, head_dim 64: two 32-dim slices per row
+    "slices_d64": lambda: small(165, batch=1, q_len=1, num_q_heads=8, num_kv_heads=2,
+                                head_dim=64, lengths=[6000]),
+    # 244 partitions (not a multiple of the 32 groups), 8 rows, head_dim 128,
+    # the shorter sequence's tail partitions empty: four slices per row
+    "slices_d128_ragged": lambda: small(166, batch=2, q_len=1, num_q_heads=4, num_kv_heads=1,
+                                        head_dim=128, fmt="bf16", lengths=[3000, 7777]),
+    # 125 partitions, 640 rows: whole rows, two rounds of loads
+    "rows_two_rounds": lambda: small(167, batch=20, q_len=2, num_q_heads=16, num_kv_heads=4,
+                                     head_dim=128, lengths=_uniform(3500, 4000, 20)),
+}
+
+
+@pytest.mark.parametrize("name", list(MERGES))
+def test_merge_forms(P, name):
+    """32-token partitions, decode and append against the oracle."""
+    case = MERGES[name]()
+    dc = DevCase(case)
+    for kind in ("decode", "append"):
+        print(f"[merge forms] {name} {kind}", flush=True)
+        ref, kc, vc = _reference(case, kind, 0)
+        if kind == "decode":
+            out = run_decode(P, dc, split=True, partition_size=32)
+        else:
+            out, k, v = run_append(P, dc, split=True, psize=32)
+            assert np.array_equal(dev_to_bits(k), kc), f"{name}: key cache differs"
+            assert np.array_equal(dev_to_bits(v), vc), f"{name}: value cache differs"
+        err = max_err(out, ref)
+        assert err <= 2e-4, f"{name} {kind}: fp32-out max abs err {err}"
