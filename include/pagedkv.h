@@ -153,7 +153,8 @@ int paged_attention_decode(void* out, int out_dtype, const void* query,
  *                     P = ceil(max_context_len / partition_size);
  *   balanced split:   (R + batch) * num_q_heads * q_len * (head_dim + 2) * 4,
  *                     R = 16384 / num_q_heads rounded down to a multiple of 8
- *                     (max_context_len plays no part).
+ *                     (max_context_len plays no part; a call uses at most R
+ *                     runs per KV head, see paged_attention_decode_splitkv).
  */
 int paged_attention_decode_splitkv_workspace_size(int batch, int q_len, int num_q_heads,
                                                   int head_dim, int max_context_len,
@@ -172,8 +173,9 @@ int paged_attention_decode_splitkv_workspace_size(int batch, int q_len, int num_
  * by paged_attention_decode_splitkv_append and
  * paged_attention_decode_splitkv_noalloc, rejected with PKV_ERR_UNSUPPORTED
  * by the other split calls).  For each KV head the batch's blocks are laid
- * end to end in sequence order and cut into R equal runs (R as for the
- * workspace size), one per wavefront, so every wavefront reads the same
+ * end to end in sequence order and cut into equal runs, one per wavefront:
+ * as many (a multiple of 8) as give the partition pass one workgroup per
+ * compute unit, at most the R of the workspace size.  Every wavefront reads the same
  * number of blocks however ragged the lengths are (mlxcel "KV Cache", Paged
  * Decode Storage and Kernels: the decode split count; here the split follows
  * the batch's total length rather than a fixed partition size).  A run that

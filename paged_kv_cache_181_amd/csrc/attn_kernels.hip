@@ -1375,24 +1375,24 @@ __global__ __launch_bounds__(kFlatMergeThreads) void attn_flat_merge_kernel(cons
   const int S = a.flat_runs;
   const int cap = a.max_blocks * kBlock;
   if (t < kWave) {                       // wave 0: T and the blocks before sequence b
-    int tot = 0, before = 0;
+    int tot = 0, before = 0, nb_b = 0;
     for (int base = 0; base < B; base += kWave) {
       const int bi = base + t;
       int L = bi < B ? a.context_lens[bi] : 0;
       L = min(max(L, 0), cap);
       const int nb = (L + kBlock - 1) / kBlock;
-      int v = nb, vb = bi < b ? nb : 0;
+      int v = nb, vb = bi < b ? nb : 0, vo = bi == b ? nb : 0;   // vo: sequence b's own
 #pragma unroll
       for (int d = 1; d < kWave; d <<= 1) {
         v += __shfl_xor(v, d, kWave);
         vb += __shfl_xor(vb, d, kWave);
+        vo += __shfl_xor(vo, d, kWave);
       }
       tot += v;
       before += vb;
+      nb_b += vo;
     }
     if (t == 0) {
-      const int L = min(max(a.context_lens[b], 0), cap);
-      const int nb_b = (L + kBlock - 1) / kBlock;
       const int per = (tot + S - 1) / S;
       int first = 0, count = 0;
       if (per > 0 && nb_b > 0) {                           // runs holding a block of b
@@ -1889,35 +1889,46 @@ static hipError_t launch_flat(const AttnArgs& a, hipStream_t stream) {
     return hipErrorInvalidValue;
   } else {
     const int rows = a.gqa * a.q_len;
+    // runs per KV head: as many as give one workgroup per compute unit (the
+    // grid is runs * Hkv / NW workgroups, whatever the heads per workgroup),
+    // a multiple of 8, at most the a.flat_runs the workspace is sized for.
+    // One round of workgroups, and fewer partials for the merge to read.
+    AttnArgs f = a;
+    const int cus = device_cu_count();
+    if (cus > 0) {
+      const int nw = rows <= 4 ? kFlatWaves<4> : kFlatWaves<16>;
+      const int want = (int)((int64_t)cus * nw / a.num_kv_heads) / 8 * 8;
+      f.flat_runs = want < 8 ? 8 : want < a.flat_runs ? want : a.flat_runs;
+    }
     // heads per workgroup: all of a workgroup's waves on one run, one head
     // each (a block's token rows of all those heads read by one CU), when the
     // KV heads divide into groups of that size; else pairs, else one head
     if (rows <= 4) {
       constexpr int NW = kFlatWaves<4>;
       const int hp = a.num_kv_heads % NW == 0 ? NW : a.num_kv_heads % 2 == 0 ? 2 : 1;
-      const dim3 grid((unsigned)(a.flat_runs / (NW / hp)), (unsigned)(a.num_kv_heads / hp));
+      const dim3 grid((unsigned)(f.flat_runs / (NW / hp)), (unsigned)(a.num_kv_heads / hp));
       if (hp == NW)
-        hipLaunchKernelGGL((attn_flat_kernel<KV, D, 4, NW>), grid, dim3(NW * kWave), 0, stream, a);
+        hipLaunchKernelGGL((attn_flat_kernel<KV, D, 4, NW>), grid, dim3(NW * kWave), 0, stream, f);
       else if (hp == 2)
-        hipLaunchKernelGGL((attn_flat_kernel<KV, D, 4, 2>), grid, dim3(NW * kWave), 0, stream, a);
+        hipLaunchKernelGGL((attn_flat_kernel<KV, D, 4, 2>), grid, dim3(NW * kWave), 0, stream, f);
       else
-        hipLaunchKernelGGL((attn_flat_kernel<KV, D, 4, 1>), grid, dim3(NW * kWave), 0, stream, a);
+        hipLaunchKernelGGL((attn_flat_kernel<KV, D, 4, 1>), grid, dim3(NW * kWave), 0, stream, f);
     } else {
       constexpr int NW = kFlatWaves<16>;
       const int hp = a.num_kv_heads % NW == 0 ? NW : a.num_kv_heads % 2 == 0 ? 2 : 1;
-      const dim3 grid((unsigned)(a.flat_runs / (NW / hp)), (unsigned)(a.num_kv_heads / hp));
+      const dim3 grid((unsigned)(f.flat_runs / (NW / hp)), (unsigned)(a.num_kv_heads / hp));
       if (hp == NW)
-        hipLaunchKernelGGL((attn_flat_kernel<KV, D, 16, NW>), grid, dim3(NW * kWave), 0, stream, a);
+        hipLaunchKernelGGL((attn_flat_kernel<KV, D, 16, NW>), grid, dim3(NW * kWave), 0, stream, f);
       else if (hp == 2)
-        hipLaunchKernelGGL((attn_flat_kernel<KV, D, 16, 2>), grid, dim3(NW * kWave), 0, stream, a);
+        hipLaunchKernelGGL((attn_flat_kernel<KV, D, 16, 2>), grid, dim3(NW * kWave), 0, stream, f);
       else
-        hipLaunchKernelGGL((attn_flat_kernel<KV, D, 16, 1>), grid, dim3(NW * kWave), 0, stream, a);
+        hipLaunchKernelGGL((attn_flat_kernel<KV, D, 16, 1>), grid, dim3(NW * kWave), 0, stream, f);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned pairs = (unsigned)((int64_t)a.batch * a.num_kv_heads);   // (sequence, KV head)
     hipLaunchKernelGGL((attn_flat_merge_kernel<D>), dim3(pairs), dim3(kFlatMergeThreads), 0,
-                       stream, a);
+                       stream, f);
     return hipGetLastError();
   }
 }

@@ -44,6 +44,12 @@ EXTRA = {
                                     head_dim=128, lengths=[5000]),
     # the ragged verify batch's shape at a quarter of its size (16-row tiles)
     "verify_b16": lambda: W.spec_verify(batch=16),
+    # G*q_len 6 at head_dim 128 and 10 at 64, one sequence over many runs
+    "slices_gq6_d128": lambda: small(174, batch=7, q_len=2, num_q_heads=6, num_kv_heads=2,
+                                     head_dim=128, fmt="bf16",
+                                     lengths=[9000, 40, 300, 2, 1200, 0, 650]),
+    "slices_gq10_d64": lambda: small(175, batch=5, q_len=2, num_q_heads=10, num_kv_heads=2,
+                                     head_dim=64, lengths=[7000, 3, 500, 64, 2222]),
 }
 _extra = {}
 
