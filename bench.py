@@ -20,6 +20,7 @@ second pass of the same work (the headline pass carries no extra events).
 
 python bench.py [--steps K] [--warmup W] [--no-extra] [--no-cpu-baseline]
 python bench.py --ceiling      # read ceiling of the 32K layer (probe library) + the kernel
+python bench.py --ceiling-k8v4 # the same for the K8/V4 batch
 """
 
 from __future__ import annotations
@@ -57,6 +58,9 @@ def parse():
     ap.add_argument("--ceiling", action="store_true",
                     help="only measure the read ceiling of the 32K layer with the probe library, "
                          "next to the partition kernel")
+    ap.add_argument("--ceiling-k8v4", action="store_true",
+                    help="only measure the read ceiling of the K8/V4 batch with the probe library, "
+                         "next to its partition kernel")
     ap.add_argument("--only", default=None,
                     help="time only this one of the other workloads (for profiling), e.g. k8v4")
     ap.add_argument("--only-partition", default=None,
@@ -329,6 +333,26 @@ OTHER = {
 WINDOW = {"long32k_window2048": 2048}       # sliding window of the windowed workloads
 
 
+def k8v4_pools(P, torch, rnd, NB, Hkv, D, layers):
+    """One K8/V4 pool per layer, every slot written by the quantize-on-write
+    path from normal draws."""
+    dev = torch.device("cuda:0")
+    pools = []
+    all_slots = torch.arange(NB * 16, dtype=torch.int64, device=dev)
+    for _ in range(layers):
+        pool = dict(k=torch.empty(NB, 16, Hkv, D, dtype=torch.int8, device=dev),
+                    ks=torch.empty(NB, 16, Hkv, dtype=torch.float16, device=dev),
+                    v=torch.empty(NB, 16, Hkv, D // 2, dtype=torch.uint8, device=dev),
+                    vs=torch.empty(NB, 16, Hkv, D // 32, dtype=torch.float16, device=dev),
+                    vz=torch.empty(NB, 16, Hkv, D // 32, dtype=torch.float16, device=dev))
+        for c0 in range(0, NB * 16, 65536):
+            sl = all_slots[c0:c0 + 65536]
+            P.kv_cache_write_k8v4(rnd(len(sl), Hkv, D), rnd(len(sl), Hkv, D), pool["k"],
+                                  pool["ks"], pool["v"], pool["vs"], pool["vz"], sl)
+        pools.append(pool)
+    return pools
+
+
 def other_workload(name, P, W, torch, steps, warmup):
     seed, layers, part = OTHER[name]
     window = WINDOW.get(name, 0)
@@ -359,19 +383,7 @@ def other_workload(name, P, W, torch, steps, warmup):
     if window:          # positions any row sees (q_len 1: the last `window` of each sequence)
         sum_len = int(sum(min(int(n), window + Q - 1) for n in lay.context_lens))
     if name == "k8v4":
-        pools = []
-        all_slots = torch.arange(NB * 16, dtype=torch.int64, device=dev)
-        for _ in range(layers):
-            pool = dict(k=torch.empty(NB, 16, Hkv, D, dtype=torch.int8, device=dev),
-                        ks=torch.empty(NB, 16, Hkv, dtype=torch.float16, device=dev),
-                        v=torch.empty(NB, 16, Hkv, D // 2, dtype=torch.uint8, device=dev),
-                        vs=torch.empty(NB, 16, Hkv, D // 32, dtype=torch.float16, device=dev),
-                        vz=torch.empty(NB, 16, Hkv, D // 32, dtype=torch.float16, device=dev))
-            for c0 in range(0, NB * 16, 65536):
-                sl = all_slots[c0:c0 + 65536]
-                P.kv_cache_write_k8v4(rnd(len(sl), Hkv, D), rnd(len(sl), Hkv, D), pool["k"],
-                                      pool["ks"], pool["v"], pool["vs"], pool["vz"], sl)
-            pools.append(pool)
+        pools = k8v4_pools(P, torch, rnd, NB, Hkv, D, layers)
         per_tok_head = D + 2 + D // 2 + 4 * (D // 32)
 
         def step():             # append form: quantize the new rows and attend, one call
@@ -587,6 +599,9 @@ PAGED_SHAPES = [
     ("all 8 heads, 8 waves x 8 blocks, 128-token partitions", 8, 8, 8, 2, 82 * 1024),
     ("all 8 heads, depth 4", 8, 8, 8, 4, 82 * 1024),
     ("all 8 heads, 16 waves x 4 blocks, depth 3", 8, 16, 8, 3, 82 * 1024),
+    ("head pairs, depth 1 (each block's loads issued after the last is folded)", 2, 8, 32, 1,
+     82 * 1024),
+    ("all 8 heads, depth 1", 8, 8, 8, 1, 82 * 1024),
 ]
 # (workgroups, waves, depth)
 STREAM_SHAPES = [(256, 8, 4), (256, 16, 4), (512, 8, 2), (512, 8, 4), (1024, 8, 2), (1024, 4, 4),
@@ -663,6 +678,91 @@ def ceiling_mode(P, W, torch, args):
     print(json.dumps({"ceiling": out}), flush=True)
 
 
+def ceiling_k8v4_mode(P, W, torch, args):
+    """Read ceiling of the K8/V4 batch (16 x 8192 tokens, 32 layers): the
+    probe library reads the same 32 layer pools with the head-group form's
+    lane addressing (one wave per KV head over a 512-token partition, the six
+    loads per block of the attention kernel), timed like the partition kernel
+    beside it (median of 32 back-to-back launches)."""
+    import statistics
+    from paged_kv_cache_181_amd import probe
+    seed, layers, part = OTHER["k8v4"]
+    lay, B, Q, Hq, Hkv, D, fmt = W.layout_of("k8v4", seed)
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed * 1000 + 7)
+    rnd = lambda *sh: torch.randn(sh, generator=gen, device=dev, dtype=torch.float16)  # noqa: E731
+    NB, G = lay.num_blocks, Hq // Hkv
+    log("building the K8/V4 pools")
+    pools = k8v4_pools(P, torch, rnd, NB, Hkv, D, layers)
+    lens = lay.context_lens.astype("int64")
+    nblk = (lens + 15) // 16
+    flat = torch.from_numpy(__import__("numpy").concatenate(
+        [lay.block_tables[b, :nblk[b]] for b in range(B)]).astype("int32")).to(dev)
+    bt = torch.from_numpy(lay.block_tables).to(dev)
+    cl = torch.from_numpy(lay.context_lens).to(dev)
+    mcl = int(lens.max())
+    q = [rnd(B, Q, Hq, D) for _ in range(layers)]
+    nbytes = P.splitkv_workspace_size(B, Q, Hq, D, mcl, part)
+    wss = [torch.zeros(nbytes // 4 + 4, dtype=torch.float32, device=dev) for _ in range(layers)]
+    out = [torch.empty(B, Q, Hq, D, dtype=torch.float16, device=dev) for _ in range(layers)]
+    sink = torch.zeros(1 << 16, dtype=torch.float32, device=dev)
+    layer_bytes = int(lens.sum()) * Hkv * (D + 2 + D // 2 + 4 * (D // 32))
+    reps = max(args.steps, 5)
+    scale = float(1.0 / D ** 0.5)
+
+    def timed(launch):
+        for l in range(layers):
+            launch(l)
+        torch.cuda.synchronize()
+        per = []
+        for _ in range(reps):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for l in range(layers):
+                launch(l)
+            e.record()
+            torch.cuda.synchronize()
+            per.append(s.elapsed_time(e) * 1e3 / layers)
+        return statistics.median(per), min(per), max(per)
+
+    def row(us, lo, hi, **kw):
+        return {**kw, "us_per_launch": round(us, 3), "us_min": round(lo, 3), "us_max": round(hi, 3),
+                "tb_per_s": round(layer_bytes / (us * 1e-6) / 1e12, 3),
+                "pct_of_hbm_peak": round(100 * layer_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2)}
+
+    res = {"workload": f"k8v4 layer pools ({B} x {mcl} tokens, {Hkv} KV heads, D {D}, "
+                       f"{layers} layers)", "bytes_per_launch": layer_bytes,
+           "launches_per_timing": layers, "timings": reps, "probe": []}
+    pblk = part // 16
+    for lds in (0, 96 * 1024):
+        for depth in (1, 2, 3, 4):
+            log(f"K8/V4 read probe: depth {depth}, LDS {lds}")
+            r = timed(lambda l: probe.k8v4_read(pools[l]["k"], pools[l]["ks"], pools[l]["v"],
+                                                pools[l]["vs"], pools[l]["vz"], flat, pblk, depth,
+                                                lds, sink))
+            res["probe"].append(row(*r, depth=depth, lds_bytes=lds,
+                                    workgroups=flat.numel() // pblk))
+    log("K8/V4 partition kernel (head groups, partition 512)")
+    r = timed(lambda l: P.paged_attention_decode_splitkv_k8v4_partials(
+        q[l], pools[l]["k"], pools[l]["ks"], pools[l]["v"], pools[l]["vs"], pools[l]["vz"], bt, cl,
+        scale, G, mcl, part, wss[l]))
+    res["partition_kernel"] = row(*r, kernel="attn_partition_kernel<K8V4,F16,128,4> head groups",
+                                  partition_size=part)
+    r = timed(lambda l: P.paged_attention_decode_splitkv_merge(out[l], mcl, part, wss[l]))
+    res["merge_kernel_us_per_launch"] = round(r[0], 3)
+    best = min(res["probe"], key=lambda x: x["us_per_launch"])
+    same = [x for x in res["probe"] if x["depth"] == 2 and x["lds_bytes"] == 96 * 1024][0]
+    k_us = res["partition_kernel"]["us_per_launch"]
+    res["summary"] = {"best_probe_us": best["us_per_launch"], "best_probe_depth": best["depth"],
+                      "best_probe_lds_bytes": best["lds_bytes"],
+                      "kernel_shape_probe_us": same["us_per_launch"],
+                      "partition_kernel_us": k_us,
+                      "kernel_frac_of_best_probe": round(best["us_per_launch"] / k_us, 4),
+                      "kernel_frac_of_its_shape": round(same["us_per_launch"] / k_us, 4)}
+    print(json.dumps({"ceiling_k8v4": res}), flush=True)
+
+
 def copy_calibration(torch):
     """A plain device copy of known size: 1 GiB read + 1 GiB written per launch.
     rocprofv3's FETCH_SIZE / WRITE_SIZE for these launches give the scale
@@ -691,6 +791,9 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration(torch)
+        return
+    if args.ceiling_k8v4:
+        ceiling_k8v4_mode(P, W, torch, args)
         return
     if args.ceiling:
         ceiling_mode(P, W, torch, args)

@@ -61,6 +61,28 @@ int pkv_probe_paged_read(const void* k_cache, const void* v_cache, const int32_t
                          int heads_per_wg, int waves, int part_blocks, int depth, int lds_bytes,
                          float* sink, size_t sink_count, void* stream);
 
+/*
+ * pkv_probe_k8v4_read — reads every K code row, V code row, K scale and V
+ * scale/zero line of `table_blocks` blocks of a K8/V4 cache (all 8 KV heads,
+ * head_dim 128; layouts as paged_attention_decode_k8v4) through the block
+ * table, with the K8/V4 head-group form's lane addressing: grid
+ * table_blocks / part_blocks workgroups of 8 wavefronts, wave g taking KV head
+ * g over the workgroup's `part_blocks` consecutive table entries; lane l
+ * (token l % 16, quarter l / 16) issues the attention kernel's six loads per
+ * block (two 16 B of the 128-byte K row, 16 B of the 64-byte V row, the 2 B
+ * K scale, the 8 B of V scales and the 8 B of V zeros), with `depth` blocks
+ * in flight (a ring of register sets).  `lds_bytes` of dynamic LDS per
+ * workgroup sets how many share a CU.  Requires num_kv_heads 8, head_dim 128,
+ * part_blocks in 1 .. 64 dividing table_blocks, depth in 1 .. 4; sink of at
+ * least 8 entries per workgroup.  A table entry outside [0, num_blocks) is
+ * not read.
+ */
+int pkv_probe_k8v4_read(const void* k_codes, const void* v_codes, const void* k_scale,
+                        const void* v_scale, const void* v_zero, const int32_t* block_table,
+                        int table_blocks, int64_t num_blocks, int num_kv_heads, int head_dim,
+                        int part_blocks, int depth, int lds_bytes, float* sink, size_t sink_count,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -162,6 +162,80 @@ void launch_paged_hp(const PagedArgs& a, dim3 grid, int waves, int depth, int ld
   launch_paged_depth<HP, 16>(a, grid, depth, lds, s);
 }
 
+// ---------------------------------------------------------------- K8/V4 paged read
+//
+// The K8/V4 head-group form's addressing at head_dim 128: one wave per KV head,
+// each walking every block of its workgroup's partition.  Lane l (token
+// rho = l % 16, quarter qd = l / 16) loads 16 B at 16 qd and at 64 + 16 qd of
+// token rho's 128-byte K code row, 16 B at 16 qd of its 64-byte V code row, the
+// token's K scale (2 B) and its four V scales and four V zeros (8 B each), six
+// loads per block as the attention kernel issues them.  A ring of DEPTH
+// register sets as in paged_read_kernel.
+struct K8Args {
+  const char *k, *v, *ks, *vs, *vz;
+  const int32_t* table;
+  int64_t num_blocks;
+  int hkv, part_blocks;
+  float* sink;
+};
+
+struct K8Set {
+  u4 k0, k1, v;
+  uint32_t ks;
+  uint32_t vs0, vs1, vz0, vz1;
+};
+
+template <int DEPTH>
+__global__ __launch_bounds__(8 * kWave) void k8v4_read_kernel(K8Args a) {
+  // (the launch's dynamic LDS only sets how many workgroups share a CU)
+  const int lane = threadIdx.x & 63;
+  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // KV head
+  const int per = a.part_blocks;
+  const int w0 = blockIdx.x * per;
+  const int tbl = lane < per ? a.table[w0 + lane] : -1;
+  const int rho = lane & 15, qd = lane >> 4;
+  const int row = rho * a.hkv + g;                                   // (token, head) row
+  const uint32_t kblk = (uint32_t)(16 * a.hkv * 128), vblk = (uint32_t)(16 * a.hkv * 64);
+  const uint32_t ksblk = (uint32_t)(16 * a.hkv * 2), vsblk = (uint32_t)(16 * a.hkv * 8);
+  const uint32_t ko = (uint32_t)(row * 128 + 16 * qd), vo = (uint32_t)(row * 64 + 16 * qd);
+  const uint32_t kso = (uint32_t)(row * 2), vso = (uint32_t)(row * 8);
+  uint32_t acc = 0;
+  K8Set set[DEPTH];
+  auto load = [&](int j, K8Set& r) {
+    const int pb = __builtin_amdgcn_readlane(tbl, j & 63);
+    const bool ok = j < per && pb >= 0 && (int64_t)pb < a.num_blocks;
+    const int64_t b = ok ? pb : 0;
+    const auto rk = rsrc(a.k + b * kblk, ok ? kblk : 0u);
+    const auto rv = rsrc(a.v + b * vblk, ok ? vblk : 0u);
+    const auto rks = rsrc(a.ks + b * ksblk, ok ? ksblk : 0u);
+    const auto rvs = rsrc(a.vs + b * vsblk, ok ? vsblk : 0u);
+    const auto rvz = rsrc(a.vz + b * vsblk, ok ? vsblk : 0u);
+    r.k0 = load16(rk, ko);
+    r.k1 = load16(rk, ko + 64);
+    r.v = load16(rv, vo);
+    r.ks = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rks, (int)kso, 0, 0);
+    const auto s2 = __builtin_amdgcn_raw_buffer_load_b64(rvs, (int)vso, 0, 0);
+    const auto z2 = __builtin_amdgcn_raw_buffer_load_b64(rvz, (int)vso, 0, 0);
+    r.vs0 = (uint32_t)s2[0];
+    r.vs1 = (uint32_t)s2[1];
+    r.vz0 = (uint32_t)z2[0];
+    r.vz1 = (uint32_t)z2[1];
+  };
+#pragma unroll
+  for (int d = 0; d < DEPTH - 1; ++d) load(d, set[d]);
+  for (int j0 = 0; j0 < per; j0 += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int fill = (d + DEPTH - 1) % DEPTH;           // the set of block j0 + d + DEPTH - 1
+      load(j0 + d + DEPTH - 1, set[fill]);
+      const K8Set& r = set[d];
+      acc ^= fold(r.k0) ^ fold(r.k1) ^ fold(r.v) ^ r.ks ^ r.vs0 ^ r.vs1 ^ r.vz0 ^ r.vz1;
+    }
+  }
+  for (int m = 1; m < kWave; m <<= 1) acc ^= (uint32_t)__shfl_xor((int)acc, m, kWave);
+  if (lane == 0) a.sink[(size_t)blockIdx.x * 8 + g] = __uint_as_float(acc);
+}
+
 template <int NW>
 void launch_stream_nw(const char* b0, const char* b1, uint32_t slice, float* sink, int wgs,
                       int depth, hipStream_t s) {
@@ -239,6 +313,35 @@ int pkv_probe_paged_read(const void* k_cache, const void* v_cache, const int32_t
     default: launch_paged_hp<8>(a, grid, waves, depth, lds_bytes, s); break;
   }
   return launched("pkv_probe_paged_read");
+}
+
+int pkv_probe_k8v4_read(const void* k_codes, const void* v_codes, const void* k_scale,
+                        const void* v_scale, const void* v_zero, const int32_t* block_table,
+                        int table_blocks, int64_t num_blocks, int num_kv_heads, int head_dim,
+                        int part_blocks, int depth, int lds_bytes, float* sink, size_t sink_count,
+                        void* stream) {
+  if (!k_codes || !v_codes || !k_scale || !v_scale || !v_zero || !block_table || !sink)
+    return fail(PKV_ERR_NULL, "a required pointer is NULL");
+  if (head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (num_kv_heads != 8) return fail(PKV_ERR_UNSUPPORTED, "num_kv_heads must be 8");
+  if (depth < 1 || depth > 4) return fail(PKV_ERR_UNSUPPORTED, "depth: 1 .. 4");
+  if (table_blocks <= 0 || part_blocks <= 0 || part_blocks > 64 || table_blocks % part_blocks)
+    return fail(PKV_ERR_SHAPE, "table_blocks must be a positive multiple of part_blocks (1 .. 64)");
+  if (num_blocks <= 0 || num_blocks * 16 * num_kv_heads * 128 > ((int64_t)1 << 40))
+    return fail(PKV_ERR_SHAPE, "num_blocks out of range");
+  if (lds_bytes < 0 || lds_bytes > 160 * 1024) return fail(PKV_ERR_SHAPE, "lds_bytes: 0 .. 160 KiB");
+  const dim3 grid((unsigned)(table_blocks / part_blocks)), blk(8 * kWave);
+  if (sink_count < (size_t)grid.x * 8) return fail(PKV_ERR_SHAPE, "sink too small");
+  K8Args a{(const char*)k_codes, (const char*)v_codes, (const char*)k_scale, (const char*)v_scale,
+           (const char*)v_zero, block_table, num_blocks, num_kv_heads, part_blocks, sink};
+  hipStream_t s = (hipStream_t)stream;
+  switch (depth) {
+    case 1: hipLaunchKernelGGL((k8v4_read_kernel<1>), grid, blk, lds_bytes, s, a); break;
+    case 2: hipLaunchKernelGGL((k8v4_read_kernel<2>), grid, blk, lds_bytes, s, a); break;
+    case 3: hipLaunchKernelGGL((k8v4_read_kernel<3>), grid, blk, lds_bytes, s, a); break;
+    default: hipLaunchKernelGGL((k8v4_read_kernel<4>), grid, blk, lds_bytes, s, a); break;
+  }
+  return launched("pkv_probe_k8v4_read");
 }
 
 }  // extern "C"

@@ -26,6 +26,8 @@ SIGNATURES = {
     "pkv_probe_last_error": ([], ctypes.c_char_p),
     "pkv_probe_stream_read": ([_p, _p, _sz, _i, _i, _i, _p, _sz, _p], _i),
     "pkv_probe_paged_read": ([_p, _p, _p, _i, _i64, _i, _i, _i, _i, _i, _i, _i, _p, _sz, _p], _i),
+    "pkv_probe_k8v4_read": ([_p, _p, _p, _p, _p, _p, _i, _i64, _i, _i, _i, _i, _i, _p, _sz, _p],
+                            _i),
 }
 for _name, (_args, _res) in SIGNATURES.items():
     getattr(lib, _name).argtypes = _args
@@ -55,3 +57,14 @@ def paged_read(k_cache, v_cache, block_table, heads_per_wg, waves, part_blocks, 
                                     block_table.numel(), nb, hkv, d, heads_per_wg, waves,
                                     part_blocks, depth, lds_bytes, _ptr(sink), sink.numel(),
                                     _stream(k_cache.device)))
+
+
+def k8v4_read(k_codes, k_scale, v_codes, v_scale, v_zero, block_table, part_blocks, depth,
+              lds_bytes, sink):
+    """Paged read of a K8/V4 cache's blocks with the head-group form's lane
+    addressing (see pagedkv_probe.h)."""
+    nb, bs, hkv, d = k_codes.shape
+    _check(lib.pkv_probe_k8v4_read(_ptr(k_codes), _ptr(v_codes), _ptr(k_scale), _ptr(v_scale),
+                                   _ptr(v_zero), _ptr(block_table), block_table.numel(), nb, hkv,
+                                   d, part_blocks, depth, lds_bytes, _ptr(sink), sink.numel(),
+                                   _stream(k_codes.device)))

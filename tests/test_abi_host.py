@@ -414,3 +414,22 @@ def test_write_validation_never_launches(P, tokens, hkv, d, bs, nb, dtype):
                                    hkv, d, bs, nb, None)
     assert rc in _NO_LAUNCH, (rc, P.last_error())
     assert rc != 0 or tokens == 0
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(vz=0), -1), (dict(head_dim=64), -3), (dict(hkv=4), -3), (dict(depth=0), -3),
+    (dict(depth=5), -3), (dict(part=65, table=65 * 4), -2), (dict(table=2047), -2),
+    (dict(nb=0), -2), (dict(lds=200 * 1024), -2), (dict(sink=8 * 64 - 1), -2),
+])
+def test_probe_k8v4_argument_errors(P, over, code):
+    """Every rejection of pkv_probe_k8v4_read comes before any launch."""
+    from paged_kv_cache_181_amd import probe
+    a = dict(k=16, v=16, ks=16, vs=16, vz=16, bt=16, table=2048, nb=2048, hkv=8, head_dim=128,
+             part=32, depth=2, lds=0, sink=8 * 64)
+    a.update(over)
+    rc = probe.lib.pkv_probe_k8v4_read(
+        *(ctypes.c_void_p(a[n]) for n in ("k", "v", "ks", "vs", "vz", "bt")), a["table"], a["nb"],
+        a["hkv"], a["head_dim"], a["part"], a["depth"], a["lds"], ctypes.c_void_p(16), a["sink"],
+        None)
+    assert rc == code, probe.lib.pkv_probe_last_error().decode()
+    assert probe.lib.pkv_probe_last_error().decode()
