@@ -1987,10 +1987,17 @@ static hipError_t launch_typed(const AttnArgs& a, hipStream_t stream, int stage)
     if constexpr (KV != Fmt::K8V4) {
       const int64_t wgs = (int64_t)a.num_parts * a.num_kv_heads * a.batch;
       const int64_t cus = device_cu_count();
-      if (rows <= 4 && a.mode == 0 && cus > 0 && wgs > cus) {
-        if (a.num_kv_heads % 2 == 0 && wgs <= 2 * cus) hp = 2;
-        else if (a.num_kv_heads % 4 == 0 && wgs <= 4 * cus) hp = 4;
-        else if (a.num_kv_heads % 8 == 0 && wgs <= 8 * cus) hp = 8;   // one wave per head
+      // h heads per workgroup (one workgroup per CU) leave about
+      // ceil(wgs / (h cus)) * h partitions of work on a CU, the one-head form
+      // (two workgroups per CU) ceil(wgs / cus): group only when that is no
+      // more, i.e. (h - 1) cus < wgs <= h cus
+      auto fits = [&](int h) {
+        return a.num_kv_heads % h == 0 && wgs > (int64_t)(h - 1) * cus && wgs <= (int64_t)h * cus;
+      };
+      if (rows <= 4 && a.mode == 0 && cus > 0) {
+        if (fits(2)) hp = 2;
+        else if (fits(4)) hp = 4;
+        else if (fits(8)) hp = 8;                                     // one wave per head
       }
     }
     if (hp > 1) {

@@ -6,7 +6,7 @@ partition's blocks and reads the run's table entries 64 at a time (one per
 lane), a chunk ahead.  The cases here give waves runs of more than 64 blocks in
 every workgroup form: one KV head per workgroup (the 32K sequence in the
 direct form and at 12288- and 16384-token partitions), head pairs and head
-quads (batches sized so that the one-head grid needs two, or up to four,
+quads (batches sized so that the one-head grid needs two, or more than three and up to four,
 workgroups per CU of a 256-CU device), in the decode, append, window and
 windowed-append calls, each against the oracle.  The spec-verify commit runs
 at the workload's full size, the K8/V4 column-group tiles run with
@@ -57,13 +57,13 @@ LONG = {
     "pairs_direct": (lambda: small(141, batch=40, q_len=1, num_q_heads=32, num_kv_heads=8,
                                    head_dim=64, fmt="bf16", lengths=_uniform(4200, 6000, 40)),
                      0, 4300),
-    # 3 x 8 x 24 = 576 workgroups: head quads, 2 waves per head x 80 blocks
-    "quads_p2560": (lambda: small(142, batch=24, q_len=1, num_q_heads=32, num_kv_heads=8,
-                                  head_dim=64, fmt="bf16", lengths=_uniform(5200, 6000, 24)),
+    # 3 x 8 x 40 = 960 workgroups: head quads, 2 waves per head x 80 blocks
+    "quads_p2560": (lambda: small(142, batch=40, q_len=1, num_q_heads=32, num_kv_heads=8,
+                                  head_dim=64, fmt="bf16", lengths=_uniform(5200, 6000, 40)),
                     2560, 5150),
-    # direct form, 80 x 8 = 640 workgroups: head quads, 65..81 blocks per wave
-    "quads_direct": (lambda: small(143, batch=80, q_len=2, num_q_heads=16, num_kv_heads=8,
-                                   head_dim=64, lengths=_uniform(2080, 2600, 80)), 0, 2090),
+    # direct form, 100 x 8 = 800 workgroups: head quads, 65..81 blocks per wave
+    "quads_direct": (lambda: small(143, batch=100, q_len=2, num_q_heads=16, num_kv_heads=8,
+                                   head_dim=64, lengths=_uniform(2080, 2600, 100)), 0, 2090),
 }
 
 
@@ -258,19 +258,22 @@ def test_k8v4_head_groups(P, name):
 
 # ------------------------------------------------------------------ 16-bit eight-head groups
 #
-# When the one-head grid needs four to eight workgroups per CU (of 256) and the
-# KV heads divide by eight, the 16-bit kernel runs eight heads per workgroup,
+# When the one-head grid needs more than seven and at most eight workgroups per
+# CU (of 256) and the KV heads divide by eight, the 16-bit kernel runs eight heads per workgroup,
 # one wavefront per head over its whole partition.
 
 EIGHTS = {
     # 32K at 128-token partitions: 256 x 8 = 2048 one-head workgroups
     "long32k_p128": (lambda: W.long32k(), 128, 2000),
-    # 10 partitions of 32 tokens x 8 heads x 20 sequences = 1600
-    "eights_b20_p32": (lambda: small(163, batch=20, q_len=1, num_q_heads=32, num_kv_heads=8,
+    # 10 partitions of 32 tokens x 8 heads x 24 sequences = 1920 (the
+    # longest sequence, 319 or 300 tokens, sets the 10 partitions)
+    "eights_b24_p32": (lambda: small(163, batch=24, q_len=1, num_q_heads=32, num_kv_heads=8,
                                      head_dim=128, fmt="bf16",
-                                     lengths=lambda r: r.integers(200, 320, size=20)), 32, 100),
-    "eights_q2_d64_p32": (lambda: small(164, batch=14, q_len=2, num_q_heads=16, num_kv_heads=8,
-                                        head_dim=64, lengths=lambda r: r.integers(2, 300, size=14)),
+                                     lengths=lambda r: np.concatenate(
+                                         [[319], r.integers(200, 320, size=23)])), 32, 100),
+    "eights_q2_d64_p32": (lambda: small(164, batch=24, q_len=2, num_q_heads=16, num_kv_heads=8,
+                                        head_dim=64, lengths=lambda r: np.concatenate(
+                                            [[300], r.integers(2, 300, size=23)])),
                           32, 40),
 }
 

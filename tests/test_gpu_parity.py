@@ -62,15 +62,17 @@ CASES = {
     # direct form (and one 512-token partition): 40 x 8 = 320 one-head workgroups
     "pairs_direct_b40": lambda: small(110, batch=40, q_len=1, num_q_heads=32, num_kv_heads=8,
                                       head_dim=64),
-    # 640 one-head workgroups (two to four per CU): the head-quad form
-    "quads_b10": lambda: small(111, batch=10, q_len=1, num_q_heads=32, num_kv_heads=8, head_dim=128,
+    # at partition 512, 8 x 8 x 14 = 896 one-head workgroups (three to four
+    # per CU): the head-quad form
+    "quads_b14": lambda: small(111, batch=14, q_len=1, num_q_heads=32, num_kv_heads=8, head_dim=128,
                                fmt="bf16", lengths=[4096, 3000, 3900, 2500, 3521, 4000, 17, 1500,
-                                                    2049, 3333]),
-    "quads_q2_d64": lambda: small(112, batch=10, q_len=2, num_q_heads=16, num_kv_heads=8,
+                                                    2049, 3333, 3700, 1, 2222, 4095]),
+    "quads_q2_d64": lambda: small(112, batch=14, q_len=2, num_q_heads=16, num_kv_heads=8,
                                   head_dim=64, lengths=[4096, 4000, 1234, 3333, 2049, 2, 3999,
-                                                        512, 513, 2800]),
-    "quads_direct_b80": lambda: small(113, batch=80, q_len=1, num_q_heads=32, num_kv_heads=8,
-                                      head_dim=64),
+                                                        512, 513, 2800, 3072, 100, 4001, 2]),
+    # one 512-token partition: 100 x 8 = 800 one-head workgroups
+    "quads_direct_b100": lambda: small(113, batch=100, q_len=1, num_q_heads=32, num_kv_heads=8,
+                                       head_dim=64),
 }
 
 _cache = {}
@@ -420,9 +422,9 @@ APPEND_CASES = {
     "pairs_b5": CASES["pairs_b5"],
     "pairs_q2_d64": CASES["pairs_q2_d64"],
     "pairs_direct_b40": CASES["pairs_direct_b40"],
-    "quads_b10": CASES["quads_b10"],
+    "quads_b14": CASES["quads_b14"],
     "quads_q2_d64": CASES["quads_q2_d64"],
-    "quads_direct_b80": CASES["quads_direct_b80"],
+    "quads_direct_b100": CASES["quads_direct_b100"],
     "long32k": lambda: W.long32k(),
 }
 
@@ -790,7 +792,7 @@ WINDOW_CASES = [
     ("small_verify_q4", 5), ("small_verify_q4", 40), ("small_g8_q2", 7), ("edge_lengths", 2),
     ("edge_lengths", 16), ("long32k", 2048), ("long32k", 4000),
     ("pairs_b5", 3900), ("pairs_q2_d64", 3800),     # head pairs at partition 512
-    ("quads_b10", 3900), ("quads_q2_d64", 3800),    # head quads at partition 512
+    ("quads_b14", 3900), ("quads_q2_d64", 3800),    # head quads at partition 512
 ]
 _window_refs = {}
 
@@ -839,7 +841,7 @@ def test_window_matches_oracle(P, name, window, split, psize):
 WINDOW_APPEND_CASES = [
     ("small_f16_d64", 1), ("small_f16_d64", 17), ("small_bf16_d128_g4", 33),
     ("small_verify_q4", 5), ("small_g8_q2", 7), ("edge_lengths", 2), ("edge_lengths", 16),
-    ("long32k", 2048), ("pairs_b5", 3900), ("pairs_q2_d64", 3800), ("quads_b10", 3900),
+    ("long32k", 2048), ("pairs_b5", 3900), ("pairs_q2_d64", 3800), ("quads_b14", 3900),
     ("quads_q2_d64", 3800),
 ]
 _window_append_refs = {}
