@@ -63,6 +63,7 @@
 //    small integers; the weights are split hi/lo).
 
 #include <math.h>
+#include <atomic>
 #include <stddef.h>
 
 #include "pkv_common.h"
@@ -1871,15 +1872,17 @@ static hipError_t launch_merge(const AttnArgs& a, hipStream_t stream) {
 
 // Compute units of the current device (0 if unknown), read once per device.
 static int device_cu_count() {
-  static int cached[64];
+  // written once per device; calls from several host threads may race to
+  // write the same value, hence the relaxed atomics
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = -1;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev] > 0 ? cached[dev] : 0;
+  return n > 0 ? n : 0;
 }
 
 // Balanced split: grid (runs / waves per head, KV heads / HP), then the merge.
