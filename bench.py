@@ -481,7 +481,8 @@ def cascade_workload(P, W, torch, steps, warmup, layers=8):
     """Shared system prompt: 8 groups of 4 sequences share a 4096-token
     prefix, each with its own 64..1024-token suffix (bf16, 32/8 heads, D 128).
     Cascade (prefix read once per group) against plain split-KV (read once
-    per sequence); both partition 1024, the fastest of 256..2048 for both."""
+    per sequence); both partition 1024 (the cascade's prefix pass; its suffix
+    pass is a balanced split), the fastest of 256..4096 for both."""
     import numpy as np
     lens, tables, NB, _, members, pre = W.shared_prefix_layout(W.rng_for(6), 8, 4, 4096, 64, 1024)
     B, Q, Hq, Hkv, D, part = 32, 1, 32, 8, 128, 1024
@@ -523,8 +524,8 @@ def cascade_workload(P, W, torch, steps, warmup, layers=8):
             "pct_of_hbm_peak": round(100 * read / (us_c * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
             "attended_gbs": round(logical / (us_c * 1e-6) / 1e9, 2),
             "layers": layers, "kv_format": "bf16",
-            "form": "cascade (prefix pass + suffix pass + merge) vs plain split-KV, partition 1024, "
-                    "HIP graph"}
+            "form": "cascade (prefix pass at 1024-token partitions + balanced suffix pass + merge) "
+                    "vs plain split-KV at 1024, HIP graph"}
 
 
 def sparse_v_workload(P, W, torch, steps, warmup, layers=32, tau=1e-3, sharpen=8.0):

@@ -333,8 +333,12 @@ int paged_attention_decode_splitkv_window_append(
  *      so group_size * gqa_factor * q_len <= 16); each row keeps its own
  *      causal limit;
  *   2. suffix pass: every sequence attends its positions from the end of its
- *      group's prefix (from 0 outside every group);
+ *      group's prefix (from 0 outside every group), as a balanced split
+ *      (paged_attention_decode_splitkv with partition_size 0) over those
+ *      suffixes: a small kernel first writes each sequence's suffix length
+ *      and first suffix table entry into the workspace;
  *   3. the log-sum-exp merge of both passes' partials.
+ *   partition_size applies to the prefix pass (a positive multiple of 16).
  *   group_members: int32 [num_groups, group_size], device; sequence indices,
  *                  -1 for an empty slot.  A sequence appears in at most one
  *                  group; a group whose first slot is -1 is ignored.
@@ -342,9 +346,15 @@ int paged_attention_decode_splitkv_window_append(
  *                  group_prefix_blocks[g] table entries must name the same
  *                  blocks (only the first member's are read).
  *   max_prefix_len: host bound on 16 * group_prefix_blocks[g] (grid size).
- * Workspace: paged_attention_decode_cascade_workspace_size bytes (prefix and
- * suffix partials side by side; contents on entry do not matter).  No window,
- * no append form.  16-bit caches only.
+ * Workspace: paged_attention_decode_cascade_workspace_size bytes: the prefix
+ * partials (batch * q_len * num_q_heads rows x P prefix partitions x
+ * (head_dim + 2) floats, P = ceil(max_prefix_len / partition_size), at least
+ * 1), then the suffix pass's balanced-split workspace (as its
+ * paged_attention_decode_splitkv_workspace_size with partition_size 0), then
+ * two int32 per sequence, each region rounded up to 256 bytes; contents on
+ * entry do not matter.  Requires what the balanced split requires
+ * (num_q_heads <= 2048, batch * max_blocks_per_seq < 2^31).  No window, no
+ * append form.  16-bit caches only.
  */
 int paged_attention_decode_cascade_workspace_size(int batch, int q_len, int num_q_heads,
                                                   int head_dim, int max_context_len,

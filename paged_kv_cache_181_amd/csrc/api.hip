@@ -500,21 +500,42 @@ int paged_attention_decode_splitkv_window_append(
                        "paged_attention_decode_splitkv_window_append");
 }
 
+// Cascade workspace: the prefix pass's partials ([rows][p_pre] slots, rows =
+// batch * q_len * num_q_heads), then the balanced suffix pass's partials,
+// then each sequence's suffix length and first suffix table entry (int32),
+// every region starting on a 256-byte boundary.
+struct CascadeLayout {
+  int64_t p_pre = 0;
+  size_t pre_bytes = 0, flat_bytes = 0, total = 0;
+};
+
+static size_t round256(size_t n) { return (n + 255) / 256 * 256; }
+
+static int cascade_layout(int batch, int q_len, int num_q_heads, int head_dim,
+                          int max_context_len, int max_prefix_len, int partition_size,
+                          CascadeLayout& c) {
+  if (max_prefix_len < 0) return fail(PKV_ERR_SHAPE, "max_prefix_len must be >= 0");
+  int rc = split_geometry(batch, q_len, num_q_heads, head_dim, max_prefix_len, partition_size,
+                          c.p_pre, c.pre_bytes);
+  if (rc) return rc;
+  int64_t parts = 0;
+  rc = split_geometry(batch, q_len, num_q_heads, head_dim, max_context_len, 0, parts,
+                      c.flat_bytes, true);
+  if (rc) return rc;
+  c.total = round256(c.pre_bytes) + round256(c.flat_bytes) + (size_t)batch * 2 * 4;
+  return PKV_OK;
+}
+
 int paged_attention_decode_cascade_workspace_size(int batch, int q_len, int num_q_heads,
                                                   int head_dim, int max_context_len,
                                                   int max_prefix_len, int partition_size,
                                                   size_t* out_bytes) {
   if (!out_bytes) return fail(PKV_ERR_NULL, "out_bytes is NULL");
-  if (max_prefix_len < 0) return fail(PKV_ERR_SHAPE, "max_prefix_len must be >= 0");
-  int64_t p_pre = 0, p_suf = 0;
-  size_t b_pre = 0, b_suf = 0;
-  int rc = split_geometry(batch, q_len, num_q_heads, head_dim, max_prefix_len, partition_size,
-                          p_pre, b_pre);
+  CascadeLayout c;
+  int rc = cascade_layout(batch, q_len, num_q_heads, head_dim, max_context_len, max_prefix_len,
+                          partition_size, c);
   if (rc) return rc;
-  rc = split_geometry(batch, q_len, num_q_heads, head_dim, max_context_len, partition_size,
-                      p_suf, b_suf);
-  if (rc) return rc;
-  *out_bytes = b_pre + b_suf;
+  *out_bytes = c.total;
   return ok();
 }
 
@@ -545,47 +566,55 @@ int paged_attention_decode_cascade(void* out, int out_dtype, const void* query,
   if (batch == 0) return ok();
   if (num_groups > 0 && (!group_members || !group_prefix_blocks))
     return fail(PKV_ERR_NULL, "group arrays are NULL");
-  int64_t p_pre = 0, p_suf = 0;
-  size_t b_pre = 0, b_suf = 0;
-  rc = split_geometry(batch, q_len, num_q_heads, head_dim, max_prefix_len, partition_size,
-                      p_pre, b_pre);
-  if (rc) return rc;
-  rc = split_geometry(batch, q_len, num_q_heads, head_dim, max_context_len, partition_size,
-                      p_suf, b_suf);
+  CascadeLayout c;
+  rc = cascade_layout(batch, q_len, num_q_heads, head_dim, max_context_len, max_prefix_len,
+                      partition_size, c);
   if (rc) return rc;
   if (!workspace) return fail(PKV_ERR_WORKSPACE, "workspace is NULL");
   if (!aligned16(workspace)) return fail(PKV_ERR_ALIGN, "workspace must be 16-byte aligned");
-  if (workspace_bytes < b_pre + b_suf)
+  if (workspace_bytes < c.total)
     return fail(PKV_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed",
-                workspace_bytes, b_pre + b_suf);
-  const int64_t rows = (int64_t)batch * q_len * num_q_heads;
-  const int64_t total = p_pre + p_suf;
-  a.ws_parts = (int)total;
-  a.part_blocks = partition_size / 16;
-  a.ws_o = (float*)workspace;
-  a.ws_m = a.ws_o + rows * total * head_dim;
-  a.ws_l = a.ws_m + rows * total;
+                workspace_bytes, c.total);
+  char* base = (char*)workspace;
+  char* flat_ws = base + round256(c.pre_bytes);
+  int32_t* suf_len = (int32_t*)(flat_ws + round256(c.flat_bytes));
+  int32_t* suf_off = suf_len + batch;
   a.grp_members = group_members;
   a.grp_prefix = group_prefix_blocks;
   a.num_groups = num_groups;
   a.group_size = group_size;
+  // the suffix pass: a balanced split over every sequence's positions past
+  // its group's prefix (checked before anything is launched)
+  pkv::AttnArgs suf = a;
+  rc = setup_split(suf, head_dim, max_context_len, 0, flat_ws, c.flat_bytes, true);
+  if (rc) return rc;
+  suf.context_lens = suf_len;
+  suf.tbl_off = suf_off;
+  const int64_t rows = (int64_t)batch * q_len * num_q_heads;
   hipError_t e = hipSuccess;
-  // 1. the shared prefixes, once per group (slots 0 .. p_pre-1; groups absent: none)
+  // 1. the shared prefixes, once per group, into their own partial slots
   if (num_groups > 0) {
     pkv::AttnArgs pre = a;
     pre.mode = 1;
-    pre.num_parts = (int)p_pre;
+    pre.num_parts = (int)c.p_pre;
+    pre.ws_parts = (int)c.p_pre;
     pre.part_base = 0;
+    pre.part_blocks = partition_size / 16;
+    pre.ws_o = (float*)base;
+    pre.ws_m = pre.ws_o + rows * c.p_pre * head_dim;
+    pre.ws_l = pre.ws_m + rows * c.p_pre;
     e = pkv::launch_attention(pre, kv_dtype, kv_dtype, head_dim, (hipStream_t)stream,
                               pkv::STAGE_PARTIALS);
     if (e != hipSuccess) return launch_result(e, "paged_attention_decode_cascade (prefix)");
+    suf.pre_o = pre.ws_o;
+    suf.pre_m = pre.ws_m;
+    suf.pre_l = pre.ws_l;
+    suf.pre_parts = (int)c.p_pre;
   }
-  // 2. every sequence past its group's prefix (slots p_pre ..), marking the
-  //    prefix slots of sequences outside every group empty; 3. the merge
-  pkv::AttnArgs suf = a;
-  suf.mode = 2;
-  suf.num_parts = (int)p_suf;
-  suf.part_base = (int)p_pre;
+  // 2. each sequence's suffix length and first suffix table entry
+  e = pkv::launch_cascade_suffix_prep(a, suf_len, suf_off, (hipStream_t)stream);
+  if (e != hipSuccess) return launch_result(e, "paged_attention_decode_cascade (suffixes)");
+  // 3. the balanced suffix pass and the merge of both passes' partials
   return launch_result(pkv::launch_attention(suf, kv_dtype, kv_dtype, head_dim,
                                              (hipStream_t)stream),
                        "paged_attention_decode_cascade");

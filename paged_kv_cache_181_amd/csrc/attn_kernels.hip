@@ -391,13 +391,10 @@ void attn_partition_kernel(const AttnArgs a) {
   const int g0 = g - hw;                                    // the workgroup's first head
   const int Q = a.q_len, G = a.gqa, GQ = G * Q, Hq = a.num_q_heads;
   const bool split = a.ws_o != nullptr;
-  // Cascade passes over shared whole-block prefixes.  Prefix pass (PREFIX,
-  // mode 1): b is a group; its S members' rows are stacked in the tile
-  // (member m's row iq*G + hl at tile row m*GQ + iq*G + hl), so the shared
-  // blocks are read once for all of them.  Suffix pass (mode 2): b is a
-  // sequence whose blocks covered by its group's prefix are skipped.
-  // Mode 0: plain.
-  const int mode = PREFIX ? 1 : a.mode;
+  // Cascade prefix pass over shared whole-block prefixes (PREFIX, mode 1):
+  // b is a group; its S members' rows are stacked in the tile (member m's row
+  // iq*G + hl at tile row m*GQ + iq*G + hl), so the shared blocks are read
+  // once for all of them.  (The suffix pass is a balanced split.)
   const int S = PREFIX ? a.group_size : 1;
   const int GQT = S * GQ;                                   // tile rows that belong to sequences
   // output (= query) row of tile row rr < GQT, or -1 for an empty member slot
@@ -458,31 +455,7 @@ void attn_partition_kernel(const AttnArgs a) {
   // L-Q+i, so nothing before lo0 (row 0's first position) is read at all,
   // and partitions are counted from lo0's block (the grid covers the window).
   const int W = a.window;
-  // suffix pass: the blocks of b's group prefix (a group counts if its first
-  // member slot names a sequence) are the prefix pass's; start after them
-  int pre_b = 0;
-  if (mode == 2) {
-    const int total = a.num_groups * a.group_size;
-    for (int base = 0; base < total; base += kWave) {
-      const int idx = base + lane;
-      const bool hit = idx < total && a.grp_members[idx] == b &&
-                       a.grp_members[(idx / a.group_size) * a.group_size] >= 0;
-      const uint64_t bal = __builtin_amdgcn_ballot_w64(hit);
-      if (bal) {
-        pre_b = a.grp_prefix[(base + __builtin_ctzll(bal)) / a.group_size];
-        break;
-      }
-    }
-    pre_b = min(max(pre_b, 0), nblk);
-    if (split && p == 0 && pre_b == 0) {      // no group: its prefix slots are empty
-      for (int idx = threadIdx.x; idx < GQ * a.part_base; idx += NW * kWave) {
-        const int64_t pi = orow_of(idx % GQ) * wsp + idx / GQ;
-        a.ws_m[pi] = kNegInf;
-        a.ws_l[pi] = 0.f;
-      }
-    }
-  }
-  const int lo0 = mode == 2 ? pre_b * kBlock : W > 0 ? max(L - Q - W + 1, 0) : 0;
+  const int lo0 = W > 0 ? max(L - Q - W + 1, 0) : 0;
   const int sb = lo0 / kBlock;
   const int bb = sb + bb_guess;                             // the partition's first block
   const int p_new = append && L > 0
@@ -1116,10 +1089,13 @@ void attn_flat_kernel(const AttnArgs a) {
   const bool append = a.new_k != nullptr;
 
   // ---- lengths, 64 sequences per chunk (lane i: sequence base + i), and
-  // the flattened end of each: ends are inclusive prefix sums of nblk
-  auto chunk_lens = [&](int base, int& len, int& end, int carry) {
+  // the flattened end of each: ends are inclusive prefix sums of nblk; with
+  // a.tbl_off, also each sequence's first table entry (a cascade's suffix
+  // pass: its lengths count from there)
+  auto chunk_lens = [&](int base, int& len, int& end, int carry, int* off) {
     const int b = base + lane;
     int L = b < B ? a.context_lens[b] : 0;
+    if (off) *off = a.tbl_off != nullptr && b < B ? min(max(a.tbl_off[b], 0), a.max_blocks) : 0;
     L = min(max(L, 0), cap);
     len = L;
     int v = (L + kBlock - 1) / kBlock;
@@ -1130,14 +1106,14 @@ void attn_flat_kernel(const AttnArgs a) {
     }
     end = carry + v;
   };
-  int base = 0, len_c = 0, end_c = 0;
-  chunk_lens(0, len_c, end_c, 0);
+  int base = 0, len_c = 0, end_c = 0, off_c = 0;
+  chunk_lens(0, len_c, end_c, 0, &off_c);
   // (readlane, not a shuffle, so the compiler knows these values are
   // wave-uniform and keeps the segment loop in scalar control flow)
   int T = __builtin_amdgcn_readlane(end_c, kWave - 1);
   for (int bb = kWave; bb < B; bb += kWave) {               // batches past 64 sequences
     int l2, e2;
-    chunk_lens(bb, l2, e2, T);
+    chunk_lens(bb, l2, e2, T, nullptr);
     T = __builtin_amdgcn_readlane(e2, kWave - 1);
   }
   const int per = (T + S - 1) / S;
@@ -1150,7 +1126,7 @@ void attn_flat_kernel(const AttnArgs a) {
     const int carry = __builtin_amdgcn_readlane(end_c, kWave - 1);
     base += kWave;
     if (base >= B) return;
-    chunk_lens(base, len_c, end_c, carry);
+    chunk_lens(base, len_c, end_c, carry, &off_c);
     past = __builtin_amdgcn_ballot_w64(base + lane < B && end_c > r0);
   }
   int b = base + __builtin_ctzll(past);
@@ -1170,7 +1146,7 @@ void attn_flat_kernel(const AttnArgs a) {
     while (b - base >= kWave) {
       const int carry = __builtin_amdgcn_readlane(end_c, kWave - 1);
       base += kWave;
-      chunk_lens(base, len_c, end_c, carry);
+      chunk_lens(base, len_c, end_c, carry, &off_c);
     }
   };
   for (int pos = r0; pos < r1;) {
@@ -1183,13 +1159,14 @@ void attn_flat_kernel(const AttnArgs a) {
       end_b = __builtin_amdgcn_readlane(end_c, b - base);
     }
     const int L = __builtin_amdgcn_readlane(len_c, b - base);
+    const int toff = __builtin_amdgcn_readlane(off_c, b - base);   // 0 without a.tbl_off
     const int start_b = end_b - (L + kBlock - 1) / kBlock;
     const int seg_end = min(r1, end_b);
     const int jb0 = pos - start_b, n = seg_end - pos;        // the segment's blocks of b
 
     // the segment's table entries (64 per chunk), query rows and new rows
-    const auto btr = span_rsrc(a.block_tables + (int64_t)b * a.max_blocks,
-                               (uint32_t)a.max_blocks * 4u);
+    const auto btr = span_rsrc(a.block_tables + (int64_t)b * a.max_blocks + toff,
+                               (uint32_t)(a.max_blocks - toff) * 4u);
     int tbl = lane < n ? buf_load<int>(btr, (uint32_t)(jb0 + lane) * 4u) : 0;
     u4 qv[QPL];
 #pragma unroll
@@ -1358,7 +1335,10 @@ void attn_flat_kernel(const AttnArgs a) {
 // lengths as the partition pass.  Thread (item, grp), item = (row, 4-dim
 // chunk), folds slots grp, grp + NG, ... into a running (max, sum, acc) with
 // their loads in flight together; the NG running states of an item are then
-// combined in LDS, as in attn_merge_kernel.
+// combined in LDS, as in attn_merge_kernel.  In a cascade (a.pre_parts > 0)
+// the rows of a sequence whose suffix starts past its group's shared prefix
+// (a.tbl_off[b] > 0) also fold the prefix pass's a.pre_parts partials of
+// their output row.
 constexpr int kFlatMergeThreads = 512;
 
 template <int D>
@@ -1367,7 +1347,7 @@ __global__ __launch_bounds__(kFlatMergeThreads) void attn_flat_merge_kernel(cons
   constexpr int NT = kFlatMergeThreads;
   __shared__ f4 acc_s[NT];
   __shared__ float m_s[NT], den_s[NT];
-  __shared__ int geo_s[2];                                  // the first slot and the slot count
+  __shared__ int geo_s[3];               // the first slot, the slot count, prefix partials
 
   const int t = threadIdx.x;
   const int Q = a.q_len, Hq = a.num_q_heads, G = a.gqa, GQ = G * Q, B = a.batch;
@@ -1376,6 +1356,9 @@ __global__ __launch_bounds__(kFlatMergeThreads) void attn_flat_merge_kernel(cons
   const int S = a.flat_runs;
   const int cap = a.max_blocks * kBlock;
   if (t < kWave) {                       // wave 0: T and the blocks before sequence b
+    // a cascade's prefix partials count for b when its suffix starts past a
+    // shared prefix (sequences outside every group have none written)
+    const int off_b = a.pre_parts > 0 && a.tbl_off != nullptr ? a.tbl_off[b] : 0;
     int tot = 0, before = 0, nb_b = 0;
     for (int base = 0; base < B; base += kWave) {
       const int bi = base + t;
@@ -1402,34 +1385,42 @@ __global__ __launch_bounds__(kFlatMergeThreads) void attn_flat_merge_kernel(cons
       }
       geo_s[0] = first + b;
       geo_s[1] = count;
+      geo_s[2] = off_b > 0 ? a.pre_parts : 0;
     }
   }
   __syncthreads();
   const int np = geo_s[1];
+  const int ntot = np + geo_s[2];                           // slots, then prefix partials
   const int NI = GQ * NC;                                   // items (at most 16 * 32 = NT)
   const int NG = NT / NI;                                   // thread groups per item
   const int item = t % NI, grp = t / NI;
   const int rr = item / NC, c = item % NC;                  // tile row, chunk
   const int64_t p0 = ((int64_t)g * (S + B) + geo_s[0]) * GQ + rr;   // the row's first partial
+  const int64_t orow = ((int64_t)b * Q + rr / G) * Hq + g * G + rr % G;   // output row
+  const int64_t pj0 = orow * a.pre_parts;                   // its prefix partials
   float m_t = kNegInf, den = 0.f;
   f4 acc = f4{0.f, 0.f, 0.f, 0.f};
   if (grp < NG) {
     constexpr int U = 8;
-    for (int q0 = grp; q0 < np; q0 += U * NG) {
+    for (int q0 = grp; q0 < ntot; q0 += U * NG) {
       float mp[U], lp[U];
       f4 op[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {      // loads first (clamped index), no branches between
-        const int64_t pi = p0 + (int64_t)min(q0 + u * NG, np - 1) * GQ;
-        mp[u] = a.ws_m[pi];
-        lp[u] = a.ws_l[pi];
-        op[u] = *(const f4*)(a.ws_o + pi * D + 4 * c);
+        const int qq = min(q0 + u * NG, ntot - 1);
+        const int64_t pi = qq < np ? p0 + (int64_t)qq * GQ : pj0 + (qq - np);
+        const float* wm = qq < np ? a.ws_m : a.pre_m;
+        const float* wl = qq < np ? a.ws_l : a.pre_l;
+        const float* wo = qq < np ? a.ws_o : a.pre_o;
+        mp[u] = wm[pi];
+        lp[u] = wl[pi];
+        op[u] = *(const f4*)(wo + pi * D + 4 * c);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) asm volatile("" : "+v"(mp[u]), "+v"(lp[u]), "+v"(op[u]));
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const bool use = q0 + u * NG < np && mp[u] != kNegInf;
+        const bool use = q0 + u * NG < ntot && mp[u] != kNegInf;
         const float m_new = use ? fmaxf(m_t, mp[u]) : m_t;
         const float e_old = m_t == kNegInf ? 0.f : fast_exp2(m_t - m_new);
         const float e_new = use ? fast_exp2(mp[u] - m_new) : 0.f;
@@ -1458,11 +1449,55 @@ __global__ __launch_bounds__(kFlatMergeThreads) void attn_flat_merge_kernel(cons
         dt += den_s[gg * NI + t] * e;
       }
     }
-    const int64_t row = ((int64_t)b * Q + rr / G) * Hq + g * G + rr % G;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      store_out(a.out, (OutT)a.out_dtype, row * D + 4 * c + r, dt > 0.f ? tot[r] / dt : 0.f);
+      store_out(a.out, (OutT)a.out_dtype, orow * D + 4 * c + r, dt > 0.f ? tot[r] / dt : 0.f);
   }
+}
+
+// Cascade with a balanced suffix pass: one thread per sequence finds its
+// group (the first group whose first slot names a sequence and that lists
+// it), scanning the member slots through LDS 256 at a time, and writes the
+// group's prefix blocks, clamped to the sequence's own blocks, and the length
+// past them.
+__global__ __launch_bounds__(256) void cascade_suffix_prep_kernel(const AttnArgs a,
+                                                                  int32_t* suf_len,
+                                                                  int32_t* suf_off) {
+  __shared__ int mem_s[256];
+  const int b = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  const int total = a.num_groups * a.group_size;
+  // the length first, so that its load overlaps the member scan
+  const int L = b < a.batch ? min(max(a.context_lens[b], 0), a.max_blocks * kBlock) : 0;
+  int pre = 0;
+  bool found = false;
+  for (int c0 = 0; c0 < total; c0 += 256) {               // every thread reaches the barriers
+    __syncthreads();
+    const int idx = c0 + (int)threadIdx.x;
+    int m = -1;
+    if (idx < total && a.grp_members[(int64_t)(idx / a.group_size) * a.group_size] >= 0)
+      m = a.grp_members[idx];
+    mem_s[threadIdx.x] = m;
+    __syncthreads();
+    const int n = min(256, total - c0);
+    for (int k = 0; k < n && !found; ++k) {
+      if (mem_s[k] == b) {
+        pre = a.grp_prefix[(c0 + k) / a.group_size];
+        found = true;
+      }
+    }
+  }
+  if (b >= a.batch) return;
+  pre = min(max(pre, 0), (L + kBlock - 1) / kBlock);
+  suf_off[b] = pre;
+  suf_len[b] = max(L - pre * kBlock, 0);
+}
+
+hipError_t launch_cascade_suffix_prep(const AttnArgs& a, int32_t* suf_len, int32_t* suf_off,
+                                      hipStream_t stream) {
+  if (a.batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(cascade_suffix_prep_kernel, dim3((unsigned)((a.batch + 255) / 256)),
+                     dim3(256), 0, stream, a, suf_len, suf_off);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------------

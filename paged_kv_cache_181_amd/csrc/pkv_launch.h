@@ -49,13 +49,18 @@ struct AttnArgs {
   int window;                    // sliding window in positions (0: the whole context)
   int ws_parts;                  // partition slots per row in the workspace
   int part_base;                 // first slot this launch's partitions write
-  int mode;                      // 0 plain, 1 cascade prefix pass, 2 cascade suffix pass
+  int mode;                      // 0 plain, 1 cascade prefix pass
   const int32_t* grp_members;    // cascade: [num_groups, group_size] sequence ids (-1: empty)
   const int32_t* grp_prefix;     // cascade: [num_groups] shared whole blocks
   int num_groups, group_size;
   float v_log2_threshold;        // sparse-V: skip V rows below 2^this of the running max
   unsigned long long* v_rows_read;   // sparse-V: optional device counter of V rows read
   int flat_runs;                 // balanced split: runs (wavefronts) per KV head; 0 = off
+  const int32_t* tbl_off;        // balanced split: [B] first table entry of each sequence (NULL: 0)
+  const float* pre_o;            // balanced merge: cascade prefix partials [B*Q*Hq, pre_parts, D]
+  const float* pre_m;            //   their running maxima [B*Q*Hq, pre_parts]
+  const float* pre_l;            //   and denominators; folded in for sequences with tbl_off > 0
+  int pre_parts;                 // 0: no prefix partials
 };
 
 // Balanced split (partition_size 0): each KV head's flattened blocks are cut
@@ -65,6 +70,13 @@ constexpr int kFlatQueryWaves = 16384;
 constexpr int flat_runs_for(int num_q_heads) {
   return num_q_heads > 0 ? (kFlatQueryWaves / num_q_heads) / 8 * 8 : 0;
 }
+
+// Cascade with a balanced suffix pass: for each sequence, the blocks of its
+// group's shared prefix (the first group whose first slot names a sequence
+// and that lists it; 0 outside every group), clamped to its own blocks, into
+// suf_off[b], and its length past them into suf_len[b].
+hipError_t launch_cascade_suffix_prep(const AttnArgs& a, int32_t* suf_len, int32_t* suf_off,
+                                      hipStream_t stream);
 
 // kv_fmt: 0 f16, 1 bf16, 3 k8v4; q_fmt: 0 f16, 1 bf16 (must equal kv_fmt unless k8v4).
 // stage: STAGE_ALL launches the partition kernel and, for the split form, the

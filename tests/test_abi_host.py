@@ -341,9 +341,15 @@ def test_gather_argument_errors(P):
 
 
 def test_cascade_workspace_and_errors(P):
-    # rows * (prefix partitions + suffix partitions) * (D + 2) * 4
-    assert P.cascade_workspace_size(32, 1, 32, 128, 5120, 4096, 512) == 32 * 32 * (8 + 10) * 130 * 4
-    assert P.cascade_workspace_size(4, 2, 8, 64, 100, 0, 16) == 4 * 2 * 8 * (1 + 7) * 66 * 4
+    # the prefix partials (rows * prefix partitions * (D + 2) floats), the
+    # balanced suffix pass's ((16384 / Hq runs + B) * Hq * Q rows of D + 2
+    # floats), then two int32 per sequence, each region on 256 bytes
+    def r256(n):
+        return (n + 255) // 256 * 256
+    want = r256(32 * 32 * 8 * 130 * 4) + r256((512 + 32) * 32 * 1 * 130 * 4) + 32 * 2 * 4
+    assert P.cascade_workspace_size(32, 1, 32, 128, 5120, 4096, 512) == want
+    want = r256(4 * 2 * 8 * 1 * 66 * 4) + r256((2048 + 4) * 8 * 2 * 66 * 4) + 4 * 2 * 4
+    assert P.cascade_workspace_size(4, 2, 8, 64, 100, 0, 16) == want
     lib = P.lib
     base = [FAKE, 0, FAKE, FAKE, FAKE, 0, FAKE, 8, FAKE, 8, 1, 32, 4, 128, 16, 64, 0.1]
     #        members, prefix, groups, size, max_prefix, max_ctx, psize, ws, bytes

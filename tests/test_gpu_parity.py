@@ -1041,6 +1041,12 @@ CASCADE_CASES = {
                                        suffix_lo=2, suffix_hi=70, num_q_heads=16,
                                        num_kv_heads=4, head_dim=128, fmt="bf16", q_len=2),
     "system_prompt": lambda: W.shared_prefix(seed=6),
+    # 40 groups of 8 = 320 sequences: more than 256 member slots (the suffix
+    # kernel scans them in two rounds, over two workgroups of sequences) and
+    # more than 64 sequences (the balanced walk's length chunks)
+    "many_groups": lambda: W.shared_prefix(seed=143, groups=40, group_size=8, prefix_len=32,
+                                           suffix_lo=1, suffix_hi=40, num_q_heads=4,
+                                           num_kv_heads=2, head_dim=64, fmt="f16"),
 }
 
 
