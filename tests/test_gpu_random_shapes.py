@@ -10,8 +10,11 @@ drawn from 16..1024, so the launcher's grid-dependent choices (head pairs,
 quads, eights, the merge's two forms, the balanced run count) meet shapes no
 hand-written case picked.  The cascade cases draw groups, group sizes, shared
 prefixes and suffixes, and clear member slots at random (sequences outside
-every group, and groups whose first slot is empty, which are ignored).
-fp32 output within 2e-4 of the fp64 oracle throughout.
+every group, and groups whose first slot is empty, which are ignored).  The
+K8/V4 cases run the quantize-on-write append form, direct and split (the code
+arrays bit-exact after the call), and the window cases the windowed decode,
+direct and split, and the windowed append form, with windows from 1 to twice
+the longest sequence.  fp32 output within 2e-4 of the fp64 oracle throughout.
 """
 
 import numpy as np
@@ -22,7 +25,8 @@ import oracle
 from paged_kv_cache_181_amd import workloads as W
 
 from gpu_util import DevCase, dev_to_bits, max_err, oracle_decode, run_decode
-from test_gpu_parity import run_append, run_cascade, small
+from test_gpu_parity import (k8v4_append_expected, run_append, run_cascade, run_k8v4_append,
+                             run_window, run_window_append, small)
 
 pytestmark = pytest.mark.gpu
 
@@ -99,3 +103,46 @@ def test_random_cascades(P, seed):
     out = run_cascade(P, DevCase(case), members, case.extra["prefix_blocks"], psize=psize)
     err = max_err(out, ref)
     assert err <= 2e-4, f"cascade seed {seed}: fp32-out max abs err {err}"
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_k8v4(P, seed):
+    case, psize = _case(100 + seed)
+    print(f"[random k8v4] seed {seed}: B {case.batch} Q {case.q_len} Hq {case.num_q_heads} "
+          f"Hkv {case.num_kv_heads} D {case.head_dim} {case.fmt} max L "
+          f"{int(case.context_lens.max())} partition {psize}", flush=True)
+    before, after, ref = k8v4_append_expected(case)
+    for split in (False, True):
+        out, arrays = run_k8v4_append(P, case, before, split=split, psize=psize)
+        for got, want in zip(arrays, after):
+            assert np.array_equal(got, want), f"k8v4 seed {seed} split {split}: arrays differ"
+        err = max_err(out, ref)
+        assert err <= 2e-4, f"k8v4 seed {seed} split {split}: fp32-out max abs err {err}"
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_windows(P, seed):
+    case, psize = _case(200 + seed)
+    r = np.random.default_rng(9700 + seed)
+    window = int(r.integers(1, 2 * max(int(case.context_lens.max()), 1) + 1))
+    print(f"[random window] seed {seed}: B {case.batch} Q {case.q_len} Hq {case.num_q_heads} "
+          f"Hkv {case.num_kv_heads} max L {int(case.context_lens.max())} window {window} "
+          f"partition {psize}", flush=True)
+    ref = oracle.paged_attention(case.query, case.key_cache, case.value_cache, case.block_tables,
+                                 case.context_lens, case.scale, case.gqa_factor, case.fmt,
+                                 window=window)
+    dc = DevCase(case)
+    for split in (False, True):
+        out = run_window(P, dc, window, split=split, psize=psize)
+        err = max_err(out, ref)
+        assert err <= 2e-4, f"window seed {seed} split {split}: fp32-out max abs err {err}"
+    slots = oracle.append_slots(case.block_tables, case.context_lens, case.q_len, case.num_blocks)
+    kc, vc = oracle.kv_cache_write(case.new_key, case.new_value, case.key_cache, case.value_cache,
+                                   slots)
+    aref = oracle.paged_attention(case.query, kc, vc, case.block_tables, case.context_lens,
+                                  case.scale, case.gqa_factor, case.fmt, window=window)
+    out, k, v = run_window_append(P, dc, window, split=True, psize=psize)
+    assert np.array_equal(dev_to_bits(k), kc), f"window seed {seed}: key cache differs"
+    assert np.array_equal(dev_to_bits(v), vc), f"window seed {seed}: value cache differs"
+    err = max_err(out, aref)
+    assert err <= 2e-4, f"window seed {seed} append: fp32-out max abs err {err}"
