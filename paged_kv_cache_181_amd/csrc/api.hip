@@ -110,9 +110,12 @@ int split_geometry(int batch, int q_len, int num_q_heads, int head_dim, int max_
     return fail(PKV_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
   if (partition_size == 0 && balanced) {
     const int runs = pkv::flat_runs_for(num_q_heads);
-    if (runs < 8 || batch > 65535)
+    if (runs < 8)
       return fail(PKV_ERR_UNSUPPORTED, "balanced split: num_q_heads must be at most %d",
                   pkv::kFlatQueryWaves / 8);
+    if (batch > 65535)
+      return fail(PKV_ERR_UNSUPPORTED, "balanced split: batch must be at most 65535 (got %d)",
+                  batch);
     parts = 0;
     bytes = (size_t)((int64_t)(runs + batch) * num_q_heads * q_len * (head_dim + 2) * 4);
     return PKV_OK;

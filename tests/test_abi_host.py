@@ -189,6 +189,13 @@ def test_splitkv_workspace_errors(P):
     assert size.value == (2728 + 3) * 6 * 4 * 66 * 4
     assert lib.paged_attention_decode_splitkv(*base, 64, 0, FAKE, (512 + 2) * 32 * 130 * 4 - 16,
                                               None) == -4
+    # its limits: at most 2048 query heads (8 runs) and 65535 sequences
+    assert lib.paged_attention_decode_splitkv_workspace_size(1, 1, 4096, 128, 64, 0,
+                                                             ctypes.byref(size)) == -3
+    assert "num_q_heads" in P.last_error()
+    assert lib.paged_attention_decode_splitkv_workspace_size(65536, 1, 32, 128, 64, 0,
+                                                             ctypes.byref(size)) == -3
+    assert "batch" in P.last_error()
     # the calls without a balanced form reject it before any launch
     assert lib.paged_attention_decode_splitkv_window(*base, 0, 64, 0, FAKE, 1 << 30, None) == -3
     assert lib.paged_attention_decode_splitkv_partials(*base[2:], 64, 0, FAKE, 1 << 30, None) == -3
