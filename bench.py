@@ -782,7 +782,7 @@ def copy_calibration(torch):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "bench.py measures one GPU; --gpus must be 1"}))
         sys.exit(2)
     import torch
     import paged_kv_cache_181_amd as P
